@@ -1,0 +1,314 @@
+"""Throughput of the fused dequantize-and-multiply path on one MI355X.
+
+Workload (one "step"): the decode product of a ~1B-parameter dense transformer
+with Q8_0 weights -- QKV 3072x2048, O 2048x2048, gate and up 6144x2048, down
+2048x6144 and the output head 65536x2048 -- at batch 1 and again at batch 8
+(Phobos README "Inference": Q8_0 ~1B models decoded on the GPU).  Weights and
+activations are seeded synthetic tensors with the model's shapes; they are
+resident in HBM before the timed region.  The weights are cycled over enough
+distinct device copies (>= 1 GiB) that no step finds its weights in the 256 MB
+last-level cache.
+
+Prints one JSON line: weight GB/s of the step (value), the dominant kernel's
+achieved bandwidth against the 8 TB/s HBM peak (roofline, timed with HIP events
+on the launch stream), and the CPU oracle's rate on a bounded sample
+(cpu_baseline).  Secondary figures (Q4_K GEMV, routed MoE, pp512 GEMM TOPS) are
+reported under "secondary" unless --no-secondary is given.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dequant-GEMV weight GB/s (% HBM peak) + pp512 quant-GEMM TOPS (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+LLC_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=0, help="weight copies to cycle (0 = auto, >= 1 GiB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--only", choices=["layerset", "q4k", "moe", "gemm"], default=None,
+                   help="run one workload only (for profiling); prints its own JSON line")
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------- #
+class Timer:
+    """Per-launch HIP events on the current stream, grouped by kernel label."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def run(self, label, nbytes, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        self.marks.append((label, nbytes, ev0, ev1))
+
+    def summary(self):
+        self.torch.cuda.synchronize()
+        agg = {}
+        for label, nbytes, a, b in self.marks:
+            ms = a.elapsed_time(b)
+            t, n, c = agg.get(label, (0.0, 0, 0))
+            agg[label] = (t + ms, n + nbytes, c + 1)
+        return agg
+
+
+def layer_set_step(g, torch, ws, xs, ys, timer=None):
+    """One pass: every matrix of the set at batch 1, then at batch 8."""
+    for b in (1, 8):
+        for (name, n, k), w in zip(ws["shapes"], ws["w"]):
+            x = xs[(name, b)]
+            y = ys[(name, b)]
+            if timer is None:
+                g.quant_gemv(g.Q8_0, w, n, k, x, y)
+            else:
+                nbytes = w.numel() + x.numel() * 4 + y.numel() * 4
+                timer.run(f"gemv_q8_0_b{b}", nbytes, lambda: g.quant_gemv(g.Q8_0, w, n, k, x, y))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard rows / experts / N-columns across GPUs; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_gguf_q8_amd as g
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    if args.only and args.only != "layerset":
+        out = secondary(g, torch, synth, only=args.only)
+        print(json.dumps(out), flush=True)
+        return
+
+    # ---- inputs: one host copy, C device copies of the weights ----
+    shapes = list(synth.DENSE_1B_LAYER_SET)
+    host_w = [synth.q8_0_matrix(n, k, seed=0, tensor_id=synth.tid(1, n, k)) for _, n, k in shapes]
+    set_bytes = sum(w.nbytes for w in host_w)
+    copies = args.copies or max(2, -(-(1 << 30) // set_bytes))
+    dev_sets = []
+    for c in range(copies):
+        ws = [torch.from_numpy(w).to(dev) for w in host_w]
+        dev_sets.append({"shapes": shapes, "w": ws})
+    del host_w
+    xs, ys = {}, {}
+    for name, n, k in shapes:
+        for b in (1, 8):
+            xs[(name, b)] = torch.from_numpy(
+                synth.normal_f32((b, k), seed=0, tensor_id=synth.tid(1, n, k) + b)).to(dev)
+            ys[(name, b)] = torch.empty((b, n), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    weight_bytes_step = 2 * set_bytes
+    for i in range(args.warmup):
+        layer_set_step(g, torch, dev_sets[i % copies], xs, ys)
+    torch.cuda.synchronize()
+
+    # ---- timed region: plain launches ----
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer_set_step(g, torch, dev_sets[i % copies], xs, ys)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = weight_bytes_step / (ms_step * 1e-3) / 1e9
+
+    # ---- per-launch HIP events over a second pass of the same steps ----
+    timer = Timer(torch)
+    for i in range(args.steps):
+        layer_set_step(g, torch, dev_sets[i % copies], xs, ys, timer)
+    agg = timer.summary()
+    dom = max(agg, key=lambda k: agg[k][0])
+    dom_ms, dom_bytes, dom_n = agg[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    per_kernel = {k: {"launches": c, "avg_us": round(t * 1e3 / c, 3),
+                      "GB/s": round(nb / (t * 1e-3) / 1e9, 1)} for k, (t, nb, c) in agg.items()}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense ~1B decode layer set, Q8_0 weights: qkv 3072x2048, o 2048x2048, "
+                        "gate 6144x2048, up 6144x2048, down 2048x6144, head 65536x2048; "
+                        "batch 1 then batch 8 per step",
+            "weight_format": "q8_0",
+            "weight_bytes_per_step": weight_bytes_step,
+            "weight_copies_cycled": copies,
+            "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launches": dom_n,
+            "avg_launch_us": round(dom_ms * 1e3 / dom_n, 3),
+        },
+        "kernels": per_kernel,
+    }
+
+    if not args.no_secondary:
+        result["secondary"] = secondary(g, torch, synth)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(synth, shapes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------- #
+def _events_time(torch, fn, reps):
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(reps):
+        fn(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / reps
+
+
+def secondary(g, torch, synth, only=None):
+    dev = torch.device("cuda:0")
+    out = {}
+    if only in (None, "q4k"):
+        res = {}
+        for name, n, k in synth.Q4K_FFN_PAIR:
+            w = synth.q4_k_matrix(n, k, seed=0, tensor_id=synth.tid(2, n, k))
+            copies = max(2, -(-(1 << 30) // w.nbytes))
+            wd = torch.from_numpy(w).to(dev)
+            cps = [wd.clone() for _ in range(copies)]
+            for b in (1, 4, 16):
+                x = torch.from_numpy(synth.normal_f32((b, k), 0, synth.tid(2, n, k) + 1)).to(dev)
+                y = torch.empty((b, n), dtype=torch.float32, device=dev)
+                f = lambda i: g.quant_gemv(g.Q4_K, cps[i % copies], n, k, x, y)
+                for i in range(10):
+                    f(i)
+                ms = _events_time(torch, f, 200)
+                gbs = w.nbytes / (ms * 1e-3) / 1e9
+                res[f"{name}_{n}x{k}_b{b}"] = {"us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                                               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            del cps, wd
+        out["q4k_gemv"] = res
+    if only in (None, "moe"):
+        res = {}
+        e, h, f, k = synth.MOE_EXPERTS, synth.MOE_HIDDEN, synth.MOE_FFN, synth.MOE_TOP_K
+        for t in (1, 16):
+            mo = synth.moe_layer(seed=0, n_tokens=t)
+            wr = torch.from_numpy(mo["wr"]).to(dev)
+            layer_bytes = mo["wg"].nbytes + mo["wu"].nbytes + mo["wd"].nbytes
+            copies = max(2, -(-(1 << 30) // layer_bytes))
+            sets = [tuple(torch.from_numpy(mo[key]).to(dev) for key in ("wg", "wu", "wd"))
+                    for _ in range(copies)]
+            x = torch.from_numpy(mo["x"]).to(dev)
+            idx, probs, _ = g.moe_route(wr, x, k)
+            ws = torch.empty(g.moe_workspace_size(e, t, k, h, f), dtype=torch.uint8, device=dev)
+            y = torch.empty((t, h), dtype=torch.float32, device=dev)
+            distinct = int(torch.unique(idx).numel())
+            per_expert = mo["wg"][0].nbytes + mo["wu"][0].nbytes + mo["wd"][0].nbytes
+            alg = distinct * per_expert + mo["wr"].nbytes
+
+            def step(i):
+                wg_, wu_, wd_ = sets[i % copies]
+                ii, pp, _ = g.moe_route(wr, x, k)
+                g.moe_expert_gemv(g.Q4_K, wg_, wu_, wd_, e, h, f, x, ii, pp, y, ws)
+
+            for i in range(10):
+                step(i)
+            ms = _events_time(torch, step, 100)
+            gbs = alg / (ms * 1e-3) / 1e9
+            res[f"t{t}"] = {"us": round(ms * 1e3, 3), "distinct_experts": distinct,
+                            "alg_bytes": alg, "GB/s": round(gbs, 1),
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            del sets
+        out["moe_q4k"] = res
+    if only in (None, "gemm"):
+        res = {}
+        m = synth.PP512_M
+        for name, fmt, n, k in synth.PP512_GEMMS:
+            tid = synth.tid(4, n, k)
+            w = torch.from_numpy(synth.quant_matrix(fmt, n, k, seed=0, tensor_id=tid)).to(dev)
+            a = torch.from_numpy(synth.normal_f32((m, k), 0, tid + 1)).to(dev)
+            c = torch.empty((m, n), dtype=torch.float32, device=dev)
+            ws = torch.empty(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
+                             device=dev)
+            f = lambda i: g.quant_gemm(fmt, w, n, k, a, c, ws)
+            for i in range(5):
+                f(i)
+            ms = _events_time(torch, f, 30)
+            tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            res[name] = {"shape": f"{m}x{n}x{k}", "us": round(ms * 1e3, 2),
+                         "TFLOP/s": round(tflops, 1),
+                         "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+        out["pp512_gemm"] = res
+    return out
+
+
+def cpu_baseline(synth, shapes, seconds):
+    """The oracle (fp64 C loops) on the same layer set, batch 1 then batch 8,
+    repeated until `seconds` of CPU time have passed (at least one full pass)."""
+    import oracle
+
+    threads = oracle.default_threads()
+    host_w = [synth.q8_0_matrix(n, k, seed=0, tensor_id=synth.tid(1, n, k)) for _, n, k in shapes]
+    xs = {(name, b): synth.normal_f32((b, k), seed=0, tensor_id=synth.tid(1, n, k) + b)
+          for name, n, k in shapes for b in (1, 8)}
+    done_bytes = 0
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for b in (1, 8):
+            for (name, n, k), w in zip(shapes, host_w):
+                oracle.gemv(synth.FMT_Q8_0, w, n, k, xs[(name, b)], threads=threads)
+                done_bytes += w.nbytes
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the layer set at batch 1 and 8 "
+                      f"({done_bytes} weight bytes) in {el:.1f} s, fp64 oracle, "
+                      f"{threads} threads over row ranges"}
+
+
+if __name__ == "__main__":
+    main()

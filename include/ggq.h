@@ -1,0 +1,177 @@
+/*
+ * ggq.h -- C ABI of the MI355X (gfx950) library for matrix products over GGUF
+ * block-quantized weights.
+ *
+ * What the calls compute, and the passages they follow:
+ *  - Phobos README (githubhelp mirror), section "Inference": quantized GGUF models
+ *    (Q8_0, Q4_K_M) run their products on the GPU at decode time; the engine
+ *    fuses kernels ("Kernel fusion, memory management" under "Components").
+ *  - Same README, opening paragraph: a mixture-of-experts layer sends each token
+ *    to a few experts and only those experts' weights are used.
+ *  - Same README, "Command-Line Tools" / phobos-bench: prompt processing is
+ *    measured at pp<N> (N-token prompts); prompt batches are matrix-matrix work.
+ *  - Kernel-cache page (phobos-lang.dev, section "Kernel cache"): one kernel per
+ *    shape and format.
+ * The pages define neither block format; this library reads them as the GGUF
+ * on-disk layout:
+ *    Q8_0: 34-byte blocks of 32 weights: fp16 d, then 32 int8 q.  w = d*q.
+ *    Q4_K: 144-byte super-blocks of 256 weights: fp16 d, fp16 dmin, 12 bytes of
+ *          packed 6-bit sub-block scales sc[8] and mins m[8], then 128 bytes of
+ *          4-bit quants.  w = d*sc*q - dmin*m.
+ *
+ * Conventions for every call:
+ *  - A quantized matrix W is N x K, row-major: row r is K/32 Q8_0 blocks
+ *    (K*34/32 bytes) or K/256 Q4_K super-blocks (K*144/256 bytes); rows are
+ *    contiguous.  Activations X are fp32 [B][K] with row stride ldx (elements);
+ *    outputs Y are fp32 [B][N] with row stride ldy.
+ *  - Every pointer is a device pointer owned by the caller (e.g. a torch tensor's
+ *    data_ptr()).  The library allocates nothing, keeps no pointer after return
+ *    and never synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL
+ *    is the default stream).
+ *  - Arguments are validated on the host before any HIP call; an invalid call
+ *    returns a negative ggq_status and enqueues nothing.  A launch failure returns
+ *    GGQ_ERR_LAUNCH.  Device faults surface at the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give the same bits, and no
+ *    floating-point atomics are used.
+ *  - Nothing throws across this interface.
+ */
+#ifndef GGQ_H
+#define GGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block formats, numbered as GGUF tensor types. */
+enum ggq_type { GGQ_Q8_0 = 8, GGQ_Q4_K = 12 };
+
+enum ggq_status {
+    GGQ_OK = 0,
+    GGQ_ERR_ARG = -1,         /* null pointer, bad size, K not a multiple of the block */
+    GGQ_ERR_UNSUPPORTED = -2, /* unknown format or mode */
+    GGQ_ERR_ALIGN = -3,       /* a pointer or leading dimension breaks the alignment rules */
+    GGQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the size query says */
+    GGQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch */
+};
+
+enum ggq_gemm_mode { GGQ_GEMM_BF16 = 0 };
+
+/* Short English text for a status code; never NULL. */
+const char *ggq_status_string(int status);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int ggq_version(void);
+
+/*
+ * quant_dequantize -- out[r][c] = w[r][c] as fp32 for an N x K quantized matrix.
+ * Follows the block definitions above.  The result is exact: Q8_0 d*q and Q4_K
+ * d*sc*q, dmin*m are exact in fp32 and the Q4_K difference is rounded once, so
+ * any correct implementation gives the same bits.
+ *   type  GGQ_Q8_0 (K % 32 == 0) or GGQ_Q4_K (K % 256 == 0)
+ *   w     device, N rows of K/32*34 or K/256*144 bytes, 16-byte aligned
+ *   out   device, N*K floats, row-major, 16-byte aligned
+ * N == 0 is a no-op.  Errors: GGQ_ERR_ARG, GGQ_ERR_UNSUPPORTED, GGQ_ERR_ALIGN.
+ */
+int quant_dequantize(int type, const void *w, int64_t n, int64_t k, float *out, void *stream);
+
+/*
+ * quant_gemv -- decode matrix-vector product, batch 1..16:
+ *     y[b][r] = sum_c w[r][c] * x[b][c]   for b < batch, r < N
+ * with the weights decoded on the fly (never materialised) and one read of W
+ * serving every batch row (README "Inference": the decode-time product).
+ * fp32 arithmetic; the result is within 1e-5 * sum_c |w x| of the exact value.
+ *   w     device, 16-byte aligned
+ *   x     device fp32 [batch][ldx], ldx >= K, 16-byte aligned, ldx % 4 == 0
+ *   y     device fp32 [batch][ldy], ldy >= N
+ *   batch 1..16
+ * N == 0 is a no-op.  Errors: GGQ_ERR_ARG (null, K not a multiple of the block,
+ * batch out of range, ld too small), GGQ_ERR_ALIGN, GGQ_ERR_UNSUPPORTED.
+ */
+int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t ldx,
+               float *y, int64_t ldy, int batch, void *stream);
+
+/*
+ * quant_gemm_workspace_size -- bytes of device workspace quant_gemm needs for
+ * these sizes (the bf16 copy of A plus tile bookkeeping).  0 on bad arguments.
+ */
+size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int mode);
+
+/*
+ * quant_gemm -- prompt-batch product (phobos-bench pp<N>):
+ *     c[i][r] = sum_c a[i][c] * w[r][c]   for i < M, r < N
+ * Activations are rounded to bf16 and weight tiles decoded to bf16 in LDS; the
+ * products accumulate in fp32 on the matrix cores.  Result within
+ * 8e-3 * sum_c |a w| of the exact value.
+ *   a     device fp32 [M][lda], lda >= K, lda % 4 == 0, 16-byte aligned
+ *   c     device fp32 [M][ldc], ldc >= N
+ *   mode  GGQ_GEMM_BF16
+ *   ws    device workspace of at least quant_gemm_workspace_size() bytes,
+ *         256-byte aligned; its contents on entry do not matter
+ * M == 0 or N == 0 is a no-op.  Errors: GGQ_ERR_ARG, GGQ_ERR_ALIGN,
+ * GGQ_ERR_WORKSPACE, GGQ_ERR_UNSUPPORTED.
+ */
+int quant_gemm(int type, const void *w, int64_t n, int64_t k, const float *a, int64_t lda,
+               int64_t m, float *c, int64_t ldc, int mode, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_route -- router of a mixture-of-experts layer (README opening paragraph):
+ *     logits[t][e] = sum_h wr[e][h] * x[t][h]   (fp32)
+ * then the top_k experts by softmax probability (equivalently by logit), in
+ * rank order, equal logits ranking the lower expert index first, and their
+ * probabilities renormalised over the selected set:
+ *     probs[t][s] = exp(l_s - l_max) / sum_{s'} exp(l_s' - l_max).
+ *   wr     device fp32 [E][H], 16-byte aligned, H % 4 == 0
+ *   x      device fp32 [T][H], 16-byte aligned
+ *   idx    device int32 [T][top_k]
+ *   probs  device fp32 [T][top_k]
+ *   logits device fp32 [T][E], written (the selection is made on these values)
+ *   1 <= top_k <= min(E, 32), 1 <= E <= 1024, H % 4 == 0.  T == 0 is a no-op.
+ * Logits must be finite for the selection to be meaningful.
+ * Errors: GGQ_ERR_ARG, GGQ_ERR_ALIGN.
+ */
+int moe_route(const float *wr, int64_t e, int64_t h, const float *x, int64_t t, int top_k,
+              int32_t *idx, float *probs, float *logits, void *stream);
+
+/*
+ * moe_workspace_size -- device workspace bytes moe_expert_gemv needs:
+ * per-expert token lists, the hidden state h [T*top_k][F] and the per-slot
+ * down-projection outputs [T*top_k][H].  0 on bad arguments.
+ */
+size_t moe_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f);
+
+/*
+ * moe_expert_gemv -- routed expert feed-forward for T tokens:
+ *     for each token t and slot s with expert e = idx[t][s]:
+ *         g = Wg[e] x_t,  u = Wu[e] x_t,  h = silu(g) * u,  d = Wd[e] h
+ *     y[t] = sum_s probs[t][s] * d_(t,s)      (summed in slot order)
+ * silu(g) = g / (1 + exp(-g)).  Only the selected experts' bytes are read: the
+ * (token, slot) pairs are grouped by expert so each selected expert's gate, up
+ * and down matrices are read once for all the tokens routed to it.
+ * Stacked expert tensors: expert e of Wg/Wu (each F x H) starts at byte
+ * e*F*(H/256)*144, expert e of Wd (H x F) at byte e*H*(F/256)*144.
+ *   type   GGQ_Q4_K or GGQ_Q8_0; H and F multiples of 256; T*top_k <= 65536
+ *   x      device fp32 [T][H];  y device fp32 [T][H]
+ *   idx    device int32 [T][top_k], each in [0, E) (out-of-range entries are
+ *          treated as expert 0 with weight 0 -- never read out of bounds)
+ *   probs  device fp32 [T][top_k]
+ *   ws     device workspace >= moe_workspace_size(E, T, top_k, H, F) bytes,
+ *          256-byte aligned.  On return ws holds h at byte offset
+ *          moe_workspace_h_offset(E, T, top_k) as fp32 [T*top_k][F].
+ * Errors: GGQ_ERR_ARG, GGQ_ERR_ALIGN, GGQ_ERR_WORKSPACE, GGQ_ERR_UNSUPPORTED.
+ */
+int moe_expert_gemv(int type, const void *wg, const void *wu, const void *wd, int64_t e,
+                    int64_t h, int64_t f, const float *x, int64_t t, const int32_t *idx,
+                    const float *probs, int top_k, float *y, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Byte offset of the hidden-state array h inside the moe_expert_gemv workspace. */
+size_t moe_workspace_h_offset(int64_t e, int64_t t, int top_k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GGQ_H */

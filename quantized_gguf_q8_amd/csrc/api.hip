@@ -1,0 +1,137 @@
+// api.hip -- the C ABI declared in include/ggq.h: argument validation on the host,
+// then one or more launches on the caller's stream.  Every check runs before any
+// HIP call, so a rejected call enqueues nothing.
+#include <limits.h>
+
+#include "ggq.h"
+#include "ggq_launch.h"
+
+namespace {
+
+constexpr int kMaxBatch = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int block_of(int type) { return type == GGQ_Q8_0 ? 32 : (type == GGQ_Q4_K ? 256 : 0); }
+
+int launched(hipError_t e) { return e == hipSuccess ? GGQ_OK : GGQ_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* ggq_status_string(int status) {
+    switch (status) {
+        case GGQ_OK: return "ok";
+        case GGQ_ERR_ARG: return "invalid argument";
+        case GGQ_ERR_UNSUPPORTED: return "unsupported format or mode";
+        case GGQ_ERR_ALIGN: return "misaligned pointer or leading dimension";
+        case GGQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case GGQ_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ggq_version(void) { return 100; }
+
+int quant_dequantize(int type, const void* w, int64_t n, int64_t k, float* out, void* stream) {
+    const int blk = block_of(type);
+    if (!blk) return GGQ_ERR_UNSUPPORTED;
+    if (n < 0 || k <= 0 || k % blk != 0) return GGQ_ERR_ARG;
+    if (n == 0) return GGQ_OK;
+    if (!w || !out) return GGQ_ERR_ARG;
+    if (!aligned(w, 16) || !aligned(out, 16)) return GGQ_ERR_ALIGN;
+    if (n * (k / 32) / 256 >= (int64_t)UINT_MAX) return GGQ_ERR_ARG;
+    return launched(ggq::launch_dequant(type, static_cast<const uint8_t*>(w), n, k, out,
+                                        as_stream(stream)));
+}
+
+int quant_gemv(int type, const void* w, int64_t n, int64_t k, const float* x, int64_t ldx,
+               float* y, int64_t ldy, int batch, void* stream) {
+    const int blk = block_of(type);
+    if (!blk) return GGQ_ERR_UNSUPPORTED;
+    if (n < 0 || k <= 0 || k % blk != 0 || k > INT_MAX || n > (int64_t)INT_MAX * 8)
+        return GGQ_ERR_ARG;
+    if (batch < 1 || batch > kMaxBatch) return GGQ_ERR_ARG;
+    if (ldx < k || ldy < n) return GGQ_ERR_ARG;
+    if (n == 0) return GGQ_OK;
+    if (!w || !x || !y) return GGQ_ERR_ARG;
+    if (!aligned(w, 16) || !aligned(x, 16) || ldx % 4 != 0 || !aligned(y, 4)) return GGQ_ERR_ALIGN;
+    return launched(ggq::launch_gemv(type, static_cast<const uint8_t*>(w), n, k, x, ldx, y, ldy,
+                                     batch, as_stream(stream)));
+}
+
+size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int mode) {
+    const int blk = block_of(type);
+    if (!blk || mode != GGQ_GEMM_BF16 || m < 0 || n < 0 || k <= 0 || k % blk != 0) return 0;
+    return ggq::gemm_workspace_bytes(type, m, n, k);
+}
+
+int quant_gemm(int type, const void* w, int64_t n, int64_t k, const float* a, int64_t lda,
+               int64_t m, float* c, int64_t ldc, int mode, void* ws, size_t ws_bytes,
+               void* stream) {
+    const int blk = block_of(type);
+    if (!blk || mode != GGQ_GEMM_BF16) return GGQ_ERR_UNSUPPORTED;
+    if (n < 0 || m < 0 || k <= 0 || k % blk != 0 || lda < k || ldc < n) return GGQ_ERR_ARG;
+    if (n > (int64_t)INT_MAX * 16 || m > (int64_t)65535 * 128) return GGQ_ERR_ARG;
+    if (m == 0 || n == 0) return GGQ_OK;
+    if (!w || !a || !c) return GGQ_ERR_ARG;
+    if (!aligned(w, 16) || !aligned(a, 16) || lda % 4 != 0 || !aligned(c, 4)) return GGQ_ERR_ALIGN;
+    if (!ws || ws_bytes < ggq::gemm_workspace_bytes(type, m, n, k)) return GGQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+    return launched(ggq::launch_gemm(type, static_cast<const uint8_t*>(w), n, k, a, lda, m, c, ldc,
+                                     ws, as_stream(stream)));
+}
+
+int moe_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t, int top_k,
+              int32_t* idx, float* probs, float* logits, void* stream) {
+    if (e < 1 || e > kMaxExperts || h < 4 || h % 4 != 0 || t < 0) return GGQ_ERR_ARG;
+    if (top_k < 1 || top_k > kMaxTopK || top_k > e) return GGQ_ERR_ARG;
+    if (t > INT_MAX) return GGQ_ERR_ARG;
+    if (t == 0) return GGQ_OK;
+    if (!wr || !x || !idx || !probs || !logits) return GGQ_ERR_ARG;
+    if (!aligned(wr, 16) || !aligned(x, 16) || !aligned(idx, 4) || !aligned(probs, 4) ||
+        !aligned(logits, 4))
+        return GGQ_ERR_ALIGN;
+    return launched(ggq::launch_route(wr, e, h, x, t, top_k, idx, probs, logits, as_stream(stream)));
+}
+
+size_t moe_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
+    if (e < 1 || e > kMaxExperts || t < 1 || top_k < 1 || top_k > kMaxTopK || h < 1 || f < 1)
+        return 0;
+    return ggq::moe_ws_bytes(e, t, top_k, h, f);
+}
+
+size_t moe_workspace_h_offset(int64_t e, int64_t t, int top_k) {
+    if (e < 1 || t < 1 || top_k < 1) return 0;
+    return ggq::moe_ws_h_offset(e, t, top_k);
+}
+
+int moe_expert_gemv(int type, const void* wg, const void* wu, const void* wd, int64_t e,
+                    int64_t h, int64_t f, const float* x, int64_t t, const int32_t* idx,
+                    const float* probs, int top_k, float* y, void* ws, size_t ws_bytes,
+                    void* stream) {
+    if (!block_of(type)) return GGQ_ERR_UNSUPPORTED;
+    if (e < 1 || e > kMaxExperts || t < 0 || top_k < 1 || top_k > kMaxTopK || top_k > e)
+        return GGQ_ERR_ARG;
+    if (h < 256 || f < 256 || h % 256 != 0 || f % 256 != 0 || h > INT_MAX || f > INT_MAX)
+        return GGQ_ERR_ARG;
+    if (t * top_k > 65536) return GGQ_ERR_ARG;
+    if (t == 0) return GGQ_OK;
+    if (!wg || !wu || !wd || !x || !idx || !probs || !y) return GGQ_ERR_ARG;
+    if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(x, 16) ||
+        !aligned(y, 4) || !aligned(idx, 4) || !aligned(probs, 4))
+        return GGQ_ERR_ALIGN;
+    if (!ws || ws_bytes < ggq::moe_ws_bytes(e, t, top_k, h, f)) return GGQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+    return launched(ggq::launch_moe(type, static_cast<const uint8_t*>(wg),
+                                    static_cast<const uint8_t*>(wu),
+                                    static_cast<const uint8_t*>(wd), e, h, f, x, t, idx, probs,
+                                    top_k, y, ws, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// ggq_device.h -- device-side helpers shared by the gfx950 kernels.
+//
+// Block formats (GGUF reading; the Phobos README, "Inference", names Q8_0 and
+// Q4_K_M but does not print their layout):
+//   Q8_0  34 bytes / 32 weights : fp16 d | 32 x int8 q                w = d*q
+//   Q4_K 144 bytes / 256 weights: fp16 d | fp16 dmin | 12 B packed 6-bit
+//                                 scales+mins | 128 B of 4-bit quants
+//                                 w = d*sc*q - dmin*m
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ggq {
+
+constexpr int kQ8_0 = 8;
+constexpr int kQ4_K = 12;
+constexpr int kQ8Bytes = 34;
+constexpr int kQ4Bytes = 144;
+
+// Bytes of one row of K weights.
+template <int FMT>
+__host__ __device__ constexpr int64_t row_bytes_dev(int64_t k) {
+    return FMT == kQ8_0 ? k / 32 * kQ8Bytes : k / 256 * kQ4Bytes;
+}
+
+// Hardware fp16 -> fp32 (v_cvt_f32_f16).  Exact for every finite input,
+// subnormals included (fp16 denormals are preserved in the default FP mode).
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    _Float16 h = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16 & 0xFFFFu));
+    return static_cast<float>(h);
+}
+
+// Q4_K packed field -> four dwords whose bytes are the 6-bit values:
+//   scl = sc[0..3], sch = sc[4..7], mnl = m[0..3], mnh = m[4..7].
+// Sub-blocks 0..3 hold all six bits in bytes 0..3 (scales) / 4..7 (mins).
+// Sub-blocks 4..7 hold their low four bits in the nibbles of bytes 8..11
+// (scale low, min high) and their top two bits in the top bits of bytes 0..3
+// (scales) / 4..7 (mins).
+struct Q4KScales {
+    uint32_t scl, sch, mnl, mnh;
+};
+
+__device__ __forceinline__ Q4KScales q4k_unpack(uint32_t s0, uint32_t s1, uint32_t s2) {
+    Q4KScales r;
+    r.scl = s0 & 0x3F3F3F3Fu;
+    r.mnl = s1 & 0x3F3F3F3Fu;
+    r.sch = (s2 & 0x0F0F0F0Fu) | (((s0 >> 6) & 0x03030303u) << 4);
+    r.mnh = ((s2 >> 4) & 0x0F0F0F0Fu) | (((s1 >> 6) & 0x03030303u) << 4);
+    return r;
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t v, int i) { return (v >> (8 * i)) & 0xFFu; }
+
+// Scale and min of sub-block j (0..7).
+__device__ __forceinline__ void q4k_sub(const Q4KScales& s, int j, uint32_t& sc, uint32_t& m) {
+    uint32_t sv = j < 4 ? s.scl : s.sch;
+    uint32_t mv = j < 4 ? s.mnl : s.mnh;
+    sc = byte_of(sv, j & 3);
+    m = byte_of(mv, j & 3);
+}
+
+// Signed byte i of v as float (one v_cvt_f32_i32 with a sign-extending byte select).
+__device__ __forceinline__ float sbyte_f(uint32_t v, int i) {
+    return static_cast<float>(static_cast<int8_t>((v >> (8 * i)) & 0xFFu));
+}
+
+// Unsigned byte i of v as float (v_cvt_f32_ubyte{i}).
+__device__ __forceinline__ float ubyte_f(uint32_t v, int i) {
+    return static_cast<float>((v >> (8 * i)) & 0xFFu);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace ggq

@@ -1,0 +1,34 @@
+// ggq_launch.h -- host-side launchers behind the C ABI (internal).
+// Arguments reaching these functions have already been validated by api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ggq {
+
+int64_t row_bytes(int type, int64_t k);
+
+hipError_t launch_dequant(int type, const uint8_t* w, int64_t n, int64_t k, float* out,
+                          hipStream_t s);
+
+hipError_t launch_gemv(int type, const uint8_t* w, int64_t n, int64_t k, const float* x,
+                       int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s);
+
+// Workspace layout of the prompt GEMM.
+size_t gemm_workspace_bytes(int type, int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm(int type, const uint8_t* w, int64_t n, int64_t k, const float* a,
+                       int64_t lda, int64_t m, float* c, int64_t ldc, void* ws, hipStream_t s);
+
+hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t,
+                        int top_k, int32_t* idx, float* probs, float* logits, hipStream_t s);
+
+size_t moe_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f);
+size_t moe_ws_h_offset(int64_t e, int64_t t, int top_k);
+hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
+                      int64_t e, int64_t h, int64_t f, const float* x, int64_t t,
+                      const int32_t* idx, const float* probs, int top_k, float* y, void* ws,
+                      hipStream_t s);
+
+}  // namespace ggq

@@ -1,0 +1,42 @@
+"""Helpers for the GPU parity tests: device transfer and tolerance checks."""
+import sys
+
+import numpy as np
+import torch
+
+GEMV_TOL = 1e-5   # |y - y_ref| <= 1e-5 * sum |w x|   (fp32 decode GEMV)
+GEMM_TOL = 8e-3   # |c - c_ref| <= 8e-3 * sum |a w|   (bf16-operand prompt GEMM)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_bound(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str) -> float:
+    """Every element within its bound; zero bound demands an exact zero.  Returns
+    the worst |err| / bound (0 when all bounds are zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    zero = bound == 0
+    assert np.all(err[zero] == 0), f"{what}: nonzero where the exact value is 0"
+    ratio = np.zeros_like(err)
+    ratio[~zero] = err[~zero] / bound[~zero]
+    worst = float(ratio.max()) if ratio.size else 0.0
+    nbad = int((ratio > 1).sum())
+    assert nbad == 0, f"{what}: {nbad} of {ratio.size} outside the bound (worst {worst:.3g}x)"
+    return worst
+
+
+def check_rel(got, ref, s, tol, what) -> float:
+    return check_bound(got, ref, tol * np.asarray(s, dtype=np.float64), what)

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/ggq.h declares, and reject
+bad arguments with the documented status before touching HIP.  Fake device
+pointers are never dereferenced: every call here fails validation (or is a
+documented no-op) on the host.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ggq.h")
+
+OK, ARG, UNSUP, ALIGN, WS = 0, -1, -2, -3, -4
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def g():
+    import quantized_gguf_q8_amd as g
+    return g
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("quant_gemv", "quant_gemm", "moe_expert_gemv", "moe_route", "quant_dequantize",
+              "quant_gemm_workspace_size", "moe_workspace_size", "moe_workspace_h_offset",
+              "ggq_status_string", "ggq_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(g):
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(g):
+    for s in (OK, ARG, UNSUP, ALIGN, WS, -5, 12345):
+        assert g._lib.ggq_status_string(s)
+    assert g._lib.ggq_status_string(ARG) == b"invalid argument"
+
+
+A16 = 0x10000          # fake, 16-byte (and 256-byte) aligned "device" addresses
+B16 = 0x20000
+C16 = 0x30000
+D16 = 0x40000
+
+
+def test_gemv_validation(g):
+    L = g._lib
+    assert L.quant_gemv(99, A16, 4, 32, B16, 32, C16, 4, 1, None) == UNSUP
+    assert L.quant_gemv(8, A16, 4, 33, B16, 33, C16, 4, 1, None) == ARG      # K % 32
+    assert L.quant_gemv(12, A16, 4, 512 + 32, B16, 544, C16, 4, 1, None) == ARG  # K % 256
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 4, 0, None) == ARG       # batch 0
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 4, 17, None) == ARG      # batch 17
+    assert L.quant_gemv(8, A16, 4, 64, B16, 32, C16, 4, 1, None) == ARG       # ldx < K
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 3, 1, None) == ARG       # ldy < N
+    assert L.quant_gemv(8, None, 4, 32, B16, 32, C16, 4, 1, None) == ARG
+    assert L.quant_gemv(8, A16, 4, 32, None, 32, C16, 4, 1, None) == ARG
+    assert L.quant_gemv(8, A16 + 2, 4, 32, B16, 32, C16, 4, 1, None) == ALIGN
+    assert L.quant_gemv(8, A16, 4, 32, B16 + 4, 32, C16, 4, 1, None) == ALIGN
+    assert L.quant_gemv(8, A16, 4, 32, B16, 34, C16, 4, 1, None) == ALIGN     # ldx % 4
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16 + 2, 4, 1, None) == ALIGN
+    assert L.quant_gemv(8, None, 0, 32, None, 32, None, 0, 1, None) == OK     # N == 0 no-op
+    assert L.quant_gemv(8, A16, -1, 32, B16, 32, C16, 4, 1, None) == ARG
+
+
+def test_dequant_validation(g):
+    L = g._lib
+    assert L.quant_dequantize(7, A16, 1, 32, B16, None) == UNSUP
+    assert L.quant_dequantize(8, A16, 1, 48, B16, None) == ARG
+    assert L.quant_dequantize(12, A16, 1, 128, B16, None) == ARG
+    assert L.quant_dequantize(8, A16, 1, 0, B16, None) == ARG
+    assert L.quant_dequantize(8, None, 1, 32, B16, None) == ARG
+    assert L.quant_dequantize(8, A16 + 8, 1, 32, B16, None) == ALIGN
+    assert L.quant_dequantize(12, A16, 0, 256, None, None) == OK
+
+
+def test_gemm_validation(g):
+    L = g._lib
+    need = L.quant_gemm_workspace_size(12, 512, 1024, 5120, 0)
+    assert need >= 512 * 5120 * 2
+    assert L.quant_gemm_workspace_size(12, 512, 1024, 5100, 0) == 0
+    assert L.quant_gemm_workspace_size(12, 512, 1024, 5120, 1) == 0
+    args = lambda **kw: dict(dict(t=12, w=A16, n=1024, k=5120, a=B16, lda=5120, m=512, c=C16,
+                                  ldc=1024, mode=0, ws=D16, wsb=need), **kw)
+
+    def call(d):
+        return L.quant_gemm(d["t"], d["w"], d["n"], d["k"], d["a"], d["lda"], d["m"], d["c"],
+                            d["ldc"], d["mode"], d["ws"], d["wsb"], None)
+
+    assert call(args(mode=3)) == UNSUP
+    assert call(args(t=2)) == UNSUP
+    assert call(args(k=5000, lda=5000)) == ARG
+    assert call(args(lda=100)) == ARG
+    assert call(args(ldc=10)) == ARG
+    assert call(args(a=None)) == ARG
+    assert call(args(a=B16 + 4)) == ALIGN
+    assert call(args(lda=5122)) == ALIGN
+    assert call(args(ws=None)) == WS
+    assert call(args(wsb=need - 1)) == WS
+    assert call(args(ws=D16 + 16)) == ALIGN
+    assert call(args(m=0, w=None, a=None, c=None, ws=None)) == OK
+
+
+def test_route_validation(g):
+    L = g._lib
+    assert L.moe_route(A16, 128, 2048, B16, 1, 0, C16, D16, D16, None) == ARG
+    assert L.moe_route(A16, 128, 2048, B16, 1, 33, C16, D16, D16, None) == ARG
+    assert L.moe_route(A16, 4, 2048, B16, 1, 5, C16, D16, D16, None) == ARG
+    assert L.moe_route(A16, 2048, 2048, B16, 1, 8, C16, D16, D16, None) == ARG
+    assert L.moe_route(A16, 128, 2046, B16, 1, 8, C16, D16, D16, None) == ARG
+    assert L.moe_route(A16, 128, 2048, B16, 1, 8, C16, D16, None, None) == ARG
+    assert L.moe_route(A16 + 4, 128, 2048, B16, 1, 8, C16, D16, D16, None) == ALIGN
+    assert L.moe_route(None, 128, 2048, None, 0, 8, None, None, None, None) == OK
+
+
+def test_moe_validation(g):
+    L = g._lib
+    need = L.moe_workspace_size(128, 16, 8, 2048, 768)
+    assert need > 16 * 8 * (2048 + 768) * 4
+    assert L.moe_workspace_size(0, 16, 8, 2048, 768) == 0
+    off = L.moe_workspace_h_offset(128, 16, 8)
+    assert off % 256 == 0 and off >= (3 * 128 + 1 + 128) * 4
+
+    def call(t=12, e=128, h=2048, f=768, tt=16, k=8, ws=D16, wsb=need, x=B16):
+        return L.moe_expert_gemv(t, A16, A16, A16, e, h, f, x, tt, C16, C16, k, C16, ws, wsb, None)
+
+    # (only failing variants are called: a valid call would launch kernels on fake pointers)
+    assert call(t=5) == UNSUP
+    assert call(h=2000) == ARG
+    assert call(f=100) == ARG
+    assert call(k=9, e=8) == ARG
+    assert call(x=None) == ARG
+    assert call(x=B16 + 8) == ALIGN
+    assert call(wsb=need - 1) == WS
+    assert call(ws=D16 + 64) == ALIGN

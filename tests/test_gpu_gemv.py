@@ -1,0 +1,173 @@
+"""GPU parity: quant_dequantize (bit-exact) and quant_gemv (1e-5 * sum|w x|)
+against the CPU oracle, through the C ABI.
+
+README "Examples" (backend_check): every device op against the host reference;
+(batch_check): a batched pass against the same rows one at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import GEMV_TOL, check_rel, dev, host, say
+from _golden import q4_k_blocks, q8_0_blocks
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+Q8, Q4 = synth.FMT_Q8_0, synth.FMT_Q4_K
+
+
+@pytest.fixture(scope="module")
+def g():
+    import quantized_gguf_q8_amd as g
+    return g
+
+
+# --------------------------------------------------------------------------- #
+# dequantize: bit-exact
+def test_fp16_scales_all_patterns_bit_exact(g):
+    """All 65536 fp16 patterns as Q8_0 scales with q = 1: the device decode keeps
+    subnormals (no flush) and matches numpy's binary16 conversion."""
+    say("dequant fp16 table")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    blocks = np.zeros((65536, 34), dtype=np.uint8)
+    blocks[:, 0:2] = bits.view(np.uint8).reshape(-1, 2)
+    blocks[:, 2] = 1
+    out = host(g.quant_dequantize(Q8, dev(blocks), 65536, 32))[:, 0]
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(out), nan)
+    assert np.array_equal(out[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_dequant_golden_blocks(g):
+    say("dequant golden")
+    for raw, expect, _ in q8_0_blocks():
+        out = host(g.quant_dequantize(Q8, dev(np.frombuffer(raw, np.uint8).copy()), 1, 32))[0]
+        assert np.array_equal(out.view(np.uint32), expect.view(np.uint32))
+    for raw, expect, _, _ in q4_k_blocks():
+        out = host(g.quant_dequantize(Q4, dev(np.frombuffer(raw, np.uint8).copy()), 1, 256))[0]
+        assert np.array_equal(out.view(np.uint32), expect.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,n,k", [(Q8, 333, 2048), (Q8, 7, 96), (Q4, 129, 2560), (Q4, 1, 256)])
+def test_dequant_random_bit_exact(g, fmt, n, k):
+    say(f"dequant fmt={fmt} n={n} k={k}")
+    w = synth.quant_matrix(fmt, n, k, seed=0, tensor_id=100 + n)
+    if fmt == Q4:   # edge scales: subnormal, zero and large d/dmin
+        blk = w.reshape(-1, 144)
+        blk[::5, 0:2] = [0x01, 0x00]
+        blk[1::7, 2:4] = [0xFF, 0x7B]
+        blk[2::11, 0:4] = 0
+    ref = oracle.dequant(fmt, w, n, k)
+    out = host(g.quant_dequantize(fmt, dev(w), n, k))
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------------------- #
+# GEMV
+def _gemv_case(g, fmt, n, k, b, seed=0, tid=1):
+    w = synth.quant_matrix(fmt, n, k, seed=seed, tensor_id=tid)
+    x = synth.normal_f32((b, k), seed=seed, tensor_id=tid + 1)
+    y = host(g.quant_gemv(fmt, dev(w), n, k, dev(x)))
+    yr, s = oracle.gemv(fmt, w, n, k, x)
+    return y, yr, s, w, x
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [
+    (Q8, 1024, 1024, 1),        # the 1024 x 1024 single-token case
+    (Q8, 37, 2304, 1), (Q8, 37, 2304, 3), (Q8, 64, 6144, 8), (Q8, 65, 512, 16),
+    (Q8, 5, 224, 1), (Q8, 9, 96, 6),            # K % 256 != 0 path
+    (Q4, 70, 2560, 1), (Q4, 70, 2560, 4), (Q4, 33, 9728, 16), (Q4, 1, 256, 2),
+    (Q4, 300, 768, 5), (Q4, 17, 11264, 13),
+])
+def test_gemv_parity(g, fmt, n, k, b):
+    say(f"gemv fmt={fmt} n={n} k={k} b={b}")
+    y, yr, s, _, _ = _gemv_case(g, fmt, n, k, b, tid=n * 7 + b)
+    worst = check_rel(y, yr, s, GEMV_TOL, f"gemv {fmt} {n}x{k} b{b}")
+    say(f"  worst err / bound = {worst:.3g}")
+
+
+@pytest.mark.parametrize("name,n,k", synth.DENSE_1B_LAYER_SET)
+@pytest.mark.parametrize("b", [1, 8])
+def test_gemv_dense_layer_set_full_size(g, name, n, k, b):
+    """The ~1B dense decode layer set (Q8_0) at batch 1 and 8, every row."""
+    say(f"gemv layer {name} {n}x{k} b={b}")
+    tid = synth.tid(1, n, k)
+    w = synth.q8_0_matrix(n, k, seed=0, tensor_id=tid)
+    x = synth.normal_f32((b, k), seed=0, tensor_id=tid + 1)
+    y = host(g.quant_gemv(Q8, dev(w), n, k, dev(x)))
+    yr, s = oracle.gemv(Q8, w, n, k, x)
+    worst = check_rel(y, yr, s, GEMV_TOL, f"{name} b{b}")
+    say(f"  worst err / bound = {worst:.3g}")
+
+
+@pytest.mark.parametrize("name,n,k", synth.Q4K_FFN_PAIR)
+@pytest.mark.parametrize("b", [1, 4, 16])
+def test_gemv_q4k_ffn_full_size(g, name, n, k, b):
+    say(f"gemv q4k {name} {n}x{k} b={b}")
+    tid = synth.tid(2, n, k)
+    w = synth.q4_k_matrix(n, k, seed=0, tensor_id=tid)
+    x = synth.normal_f32((b, k), seed=0, tensor_id=tid + 1)
+    y = host(g.quant_gemv(Q4, dev(w), n, k, dev(x)))
+    yr, s = oracle.gemv(Q4, w, n, k, x)
+    worst = check_rel(y, yr, s, GEMV_TOL, f"{name} b{b}")
+    say(f"  worst err / bound = {worst:.3g}")
+
+
+def test_gemv_one_hot_columns_exact(g):
+    """x = e_c gives the dequantized column c exactly (adds of zero are exact)."""
+    say("gemv one-hot")
+    for fmt, n, k in ((Q8, 96, 2048), (Q4, 96, 2560)):
+        w = synth.quant_matrix(fmt, n, k, seed=3, tensor_id=71)
+        cols = [0, 31, 32, 255, 256, 1023, k - 1]
+        x = np.zeros((len(cols), k), dtype=np.float32)
+        for i, c in enumerate(cols):
+            x[i, c] = 1.0
+        y = host(g.quant_gemv(fmt, dev(w), n, k, dev(x)))
+        dense = oracle.dequant(fmt, w, n, k)
+        for i, c in enumerate(cols):
+            assert np.array_equal(y[i], dense[:, c])
+
+
+def test_gemv_batch_equals_single_rows_and_is_deterministic(g):
+    say("gemv batch_check")
+    for fmt, n, k in ((Q8, 200, 2048), (Q4, 200, 2560)):
+        w = synth.quant_matrix(fmt, n, k, seed=4, tensor_id=72)
+        x = synth.normal_f32((16, k), seed=4, tensor_id=73)
+        wd, xd = dev(w), dev(x)
+        yb = host(g.quant_gemv(fmt, wd, n, k, xd))
+        yb2 = host(g.quant_gemv(fmt, wd, n, k, xd))
+        assert np.array_equal(yb, yb2)
+        yr, s = oracle.gemv(fmt, w, n, k, x)
+        for b in range(16):
+            y1 = host(g.quant_gemv(fmt, wd, n, k, dev(x[b:b + 1])))
+            check_rel(y1, yr[b:b + 1], s[b:b + 1], GEMV_TOL, f"single row {b}")
+            check_rel(yb[b:b + 1], yr[b:b + 1], s[b:b + 1], GEMV_TOL, f"batched row {b}")
+
+
+def test_gemv_integer_case_exact(g):
+    """d = 1 and small integer activations: every partial sum is an exact integer."""
+    say("gemv integer exact")
+    n, k = 130, 4096
+    rng = np.random.default_rng(11)
+    q = rng.integers(-127, 128, size=(n, k))
+    raw = np.zeros((n * k // 32, 34), dtype=np.uint8)
+    raw[:, 0:2] = [0x00, 0x3C]
+    raw[:, 2:] = q.reshape(-1, 32).astype(np.int8).view(np.uint8)
+    x = rng.integers(-8, 9, size=(4, k)).astype(np.float32)
+    y = host(g.quant_gemv(Q8, dev(raw.reshape(n, -1)), n, k, dev(x)))
+    ref = (x.astype(np.int64) @ q.T).astype(np.float32)
+    assert np.array_equal(y, ref)
+
+
+def test_gemv_empty_and_errors(g):
+    say("gemv edge")
+    w = dev(np.zeros(34, dtype=np.uint8))
+    y = g.quant_gemv(Q8, w, 0, 32, dev(np.zeros((1, 32), np.float32)))
+    assert y.shape == (1, 0)
+    with pytest.raises(g.GGQError):
+        g.quant_gemv(Q8, dev(np.zeros(17 * 34, np.uint8)), 1, 17 * 32 + 16,
+                     dev(np.zeros((1, 17 * 32 + 16), np.float32)))
