@@ -1,19 +1,21 @@
 """Throughput of the fused dequantize-and-multiply path on one MI355X.
 
-Workload (one "step"): the decode product of a ~1B-parameter dense transformer
+Workload (one "step"): the decode products of a ~1B-parameter dense transformer
 with Q8_0 weights -- QKV 3072x2048, O 2048x2048, gate and up 6144x2048, down
 2048x6144 and the output head 65536x2048 -- at batch 1 and again at batch 8
-(Phobos README "Inference": Q8_0 ~1B models decoded on the GPU).  Weights and
-activations are seeded synthetic tensors with the model's shapes; they are
-resident in HBM before the timed region.  The weights are cycled over enough
-distinct device copies (>= 1 GiB) that no step finds its weights in the 256 MB
-last-level cache.
+(Phobos README "Inference": Q8_0 ~1B models decoded on the GPU).  Each batch
+size is one grouped launch over the six matrices (README "Components": kernel
+fusion).  Weights and activations are seeded synthetic tensors with the model's
+shapes, resident in HBM before the timed region.  The weights are cycled over
+enough distinct device copies (>= 1 GiB) that no step finds them in the 256 MB
+last-level cache.  Steps are replayed from HIP graphs (one per weight copy) so the
+host's launch cost is not what is measured.
 
 Prints one JSON line: weight GB/s of the step (value), the dominant kernel's
-achieved bandwidth against the 8 TB/s HBM peak (roofline, timed with HIP events
-on the launch stream), and the CPU oracle's rate on a bounded sample
-(cpu_baseline).  Secondary figures (Q4_K GEMV, routed MoE, pp512 GEMM TOPS) are
-reported under "secondary" unless --no-secondary is given.
+achieved bandwidth against the 8 TB/s HBM peak (roofline; per-launch HIP events on
+the launch stream), and the CPU oracle's rate on a bounded sample (cpu_baseline).
+Secondary figures (Q4_K GEMV, routed MoE, pp512 GEMM TFLOP/s) are reported under
+"secondary" unless --no-secondary is given.
 """
 from __future__ import annotations
 
@@ -23,75 +25,67 @@ import os
 import sys
 import time
 
-import numpy as np
-
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "dequant-GEMV weight GB/s (% HBM peak) + pp512 quant-GEMM TOPS (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-LLC_BYTES = 256 << 20
+ROTATE_BYTES = 1 << 30
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=300)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--copies", type=int, default=0, help="weight copies to cycle (0 = auto, >= 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--only", choices=["layerset", "q4k", "moe", "gemm"], default=None,
-                   help="run one workload only (for profiling); prints its own JSON line")
+    p.add_argument("--only", choices=["q4k", "moe", "gemm"], default=None,
+                   help="run one secondary workload only (for profiling)")
     return p.parse_args()
 
 
-# --------------------------------------------------------------------------- #
-class Timer:
-    """Per-launch HIP events on the current stream, grouped by kernel label."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.marks = []
-
-    def run(self, label, nbytes, fn):
-        ev0 = self.torch.cuda.Event(enable_timing=True)
-        ev1 = self.torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        fn()
-        ev1.record()
-        self.marks.append((label, nbytes, ev0, ev1))
-
-    def summary(self):
-        self.torch.cuda.synchronize()
-        agg = {}
-        for label, nbytes, a, b in self.marks:
-            ms = a.elapsed_time(b)
-            t, n, c = agg.get(label, (0.0, 0, 0))
-            agg[label] = (t + ms, n + nbytes, c + 1)
-        return agg
+def capture(torch, fns):
+    """One HIP graph per closure (each closure launches on the current stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for f in fns:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            f()
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    return graphs
 
 
-def layer_set_step(g, torch, ws, xs, ys, timer=None):
-    """One pass: every matrix of the set at batch 1, then at batch 8."""
-    for b in (1, 8):
-        for (name, n, k), w in zip(ws["shapes"], ws["w"]):
-            x = xs[(name, b)]
-            y = ys[(name, b)]
-            if timer is None:
-                g.quant_gemv(g.Q8_0, w, n, k, x, y)
-            else:
-                nbytes = w.numel() + x.numel() * 4 + y.numel() * 4
-                timer.run(f"gemv_q8_0_b{b}", nbytes, lambda: g.quant_gemv(g.Q8_0, w, n, k, x, y))
+def replay_ms(torch, graphs, reps, per_graph=1):
+    for i in range(min(len(graphs), 3)):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * per_graph)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path would shard rows / experts / N-columns across GPUs; see DESIGN.md)",
+              "(the path would shard rows, experts or output columns across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -103,20 +97,16 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
-    if args.only and args.only != "layerset":
-        out = secondary(g, torch, synth, only=args.only)
-        print(json.dumps(out), flush=True)
+    if args.only:
+        print(json.dumps(secondary(g, torch, synth, only=args.only)), flush=True)
         return
 
-    # ---- inputs: one host copy, C device copies of the weights ----
+    # ---- inputs: one host copy of the weights, C device copies ----
     shapes = list(synth.DENSE_1B_LAYER_SET)
     host_w = [synth.q8_0_matrix(n, k, seed=0, tensor_id=synth.tid(1, n, k)) for _, n, k in shapes]
     set_bytes = sum(w.nbytes for w in host_w)
-    copies = args.copies or max(2, -(-(1 << 30) // set_bytes))
-    dev_sets = []
-    for c in range(copies):
-        ws = [torch.from_numpy(w).to(dev) for w in host_w]
-        dev_sets.append({"shapes": shapes, "w": ws})
+    copies = args.copies or max(2, -(-ROTATE_BYTES // set_bytes))
+    dev_sets = [[torch.from_numpy(w).to(dev) for w in host_w] for _ in range(copies)]
     del host_w
     xs, ys = {}, {}
     for name, n, k in shapes:
@@ -124,32 +114,61 @@ def main():
             xs[(name, b)] = torch.from_numpy(
                 synth.normal_f32((b, k), seed=0, tensor_id=synth.tid(1, n, k) + b)).to(dev)
             ys[(name, b)] = torch.empty((b, n), dtype=torch.float32, device=dev)
+    groups = []   # per copy: (batch-1 group, batch-8 group)
+    for ws in dev_sets:
+        groups.append(tuple(
+            g.GemvGroup(g.Q8_0, [(w, n, k, xs[(name, b)], ys[(name, b)])
+                                 for (name, n, k), w in zip(shapes, ws)]) for b in (1, 8)))
     torch.cuda.synchronize()
-
     weight_bytes_step = 2 * set_bytes
+
+    def step_fn(c):
+        g1, g8 = groups[c]
+        return lambda: (g1(), g8())
+
+    graphs = capture(torch, [step_fn(c) for c in range(copies)])
     for i in range(args.warmup):
-        layer_set_step(g, torch, dev_sets[i % copies], xs, ys)
+        graphs[i % copies].replay()
     torch.cuda.synchronize()
 
-    # ---- timed region: plain launches ----
+    # ---- timed region: graph replays of K steps ----
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        layer_set_step(g, torch, dev_sets[i % copies], xs, ys)
+        graphs[i % copies].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = weight_bytes_step / (ms_step * 1e-3) / 1e9
 
-    # ---- per-launch HIP events over a second pass of the same steps ----
-    timer = Timer(torch)
+    # ---- per-launch HIP events on the launch stream (eager, same launches) ----
+    agg = {}
+    alg = {}
+    for b_i, label in ((0, "gemv_q8_0_grouped_b1"), (1, "gemv_q8_0_grouped_b8")):
+        grp0 = groups[0][b_i]
+        alg[label] = grp0.weight_bytes + sum(
+            xs[(name, grp0.batch)].numel() * 4 + ys[(name, grp0.batch)].numel() * 4
+            for name, _, _ in shapes)
+    evs = []
     for i in range(args.steps):
-        layer_set_step(g, torch, dev_sets[i % copies], xs, ys, timer)
-    agg = timer.summary()
+        for b_i, label in ((0, "gemv_q8_0_grouped_b1"), (1, "gemv_q8_0_grouped_b8")):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            groups[i % copies][b_i]()
+            e1.record()
+            evs.append((label, e0, e1))
+    torch.cuda.synchronize()
+    for label, e0, e1 in evs:
+        t, c = agg.get(label, (0.0, 0))
+        agg[label] = (t + e0.elapsed_time(e1), c + 1)
     dom = max(agg, key=lambda k: agg[k][0])
-    dom_ms, dom_bytes, dom_n = agg[dom]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dom_ms, dom_n = agg[dom]
+    avg_ms = dom_ms / dom_n
+    achieved = alg[dom] / (avg_ms * 1e-3) / 1e9
     per_kernel = {k: {"launches": c, "avg_us": round(t * 1e3 / c, 3),
-                      "GB/s": round(nb / (t * 1e-3) / 1e9, 1)} for k, (t, nb, c) in agg.items()}
+                      "alg_bytes": alg[k], "GB/s": round(alg[k] / (t / c * 1e-3) / 1e9, 1)}
+                  for k, (t, c) in agg.items()}
 
     result = {
         "metric": METRIC,
@@ -167,7 +186,7 @@ def main():
         "config": {
             "workload": "dense ~1B decode layer set, Q8_0 weights: qkv 3072x2048, o 2048x2048, "
                         "gate 6144x2048, up 6144x2048, down 2048x6144, head 65536x2048; "
-                        "batch 1 then batch 8 per step",
+                        "batch 1 then batch 8 per step, one grouped launch per batch",
             "weight_format": "q8_0",
             "weight_bytes_per_step": weight_bytes_step,
             "weight_copies_cycled": copies,
@@ -181,12 +200,13 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
+            "alg_bytes_per_launch": alg[dom],
+            "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches": dom_n,
-            "avg_launch_us": round(dom_ms * 1e3 / dom_n, 3),
         },
         "kernels": per_kernel,
     }
-
+    del graphs
     if not args.no_secondary:
         result["secondary"] = secondary(g, torch, synth)
     if not args.no_cpu_baseline:
@@ -195,17 +215,6 @@ def main():
 
 
 # --------------------------------------------------------------------------- #
-def _events_time(torch, fn, reps):
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(reps):
-        fn(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / reps
-
-
 def secondary(g, torch, synth, only=None):
     dev = torch.device("cuda:0")
     out = {}
@@ -213,19 +222,22 @@ def secondary(g, torch, synth, only=None):
         res = {}
         for name, n, k in synth.Q4K_FFN_PAIR:
             w = synth.q4_k_matrix(n, k, seed=0, tensor_id=synth.tid(2, n, k))
-            copies = max(2, -(-(1 << 30) // w.nbytes))
+            copies = max(2, -(-ROTATE_BYTES // w.nbytes))
             wd = torch.from_numpy(w).to(dev)
             cps = [wd.clone() for _ in range(copies)]
             for b in (1, 4, 16):
                 x = torch.from_numpy(synth.normal_f32((b, k), 0, synth.tid(2, n, k) + 1)).to(dev)
                 y = torch.empty((b, n), dtype=torch.float32, device=dev)
-                f = lambda i: g.quant_gemv(g.Q4_K, cps[i % copies], n, k, x, y)
-                for i in range(10):
-                    f(i)
-                ms = _events_time(torch, f, 200)
+                calls = [g.GemvGroup(g.Q4_K, [(c, n, k, x, y)]) for c in cps]
+                per = 16
+                fns = [(lambda j0: (lambda: [calls[(j0 + j) % copies]() for j in range(per)]))(j0)
+                       for j0 in range(0, copies, per)]
+                graphs = capture(torch, fns)
+                ms = replay_ms(torch, graphs, 4 * len(graphs), per)
                 gbs = w.nbytes / (ms * 1e-3) / 1e9
                 res[f"{name}_{n}x{k}_b{b}"] = {"us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
                                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                del graphs
             del cps, wd
         out["q4k_gemv"] = res
     if only in (None, "moe"):
@@ -235,30 +247,31 @@ def secondary(g, torch, synth, only=None):
             mo = synth.moe_layer(seed=0, n_tokens=t)
             wr = torch.from_numpy(mo["wr"]).to(dev)
             layer_bytes = mo["wg"].nbytes + mo["wu"].nbytes + mo["wd"].nbytes
-            copies = max(2, -(-(1 << 30) // layer_bytes))
+            copies = max(2, -(-ROTATE_BYTES // layer_bytes))
             sets = [tuple(torch.from_numpy(mo[key]).to(dev) for key in ("wg", "wu", "wd"))
                     for _ in range(copies)]
             x = torch.from_numpy(mo["x"]).to(dev)
-            idx, probs, _ = g.moe_route(wr, x, k)
+            idx0, _, _ = g.moe_route(wr, x, k)
+            distinct = int(torch.unique(idx0).numel())
             ws = torch.empty(g.moe_workspace_size(e, t, k, h, f), dtype=torch.uint8, device=dev)
             y = torch.empty((t, h), dtype=torch.float32, device=dev)
-            distinct = int(torch.unique(idx).numel())
             per_expert = mo["wg"][0].nbytes + mo["wu"][0].nbytes + mo["wd"][0].nbytes
             alg = distinct * per_expert + mo["wr"].nbytes
 
-            def step(i):
-                wg_, wu_, wd_ = sets[i % copies]
-                ii, pp, _ = g.moe_route(wr, x, k)
-                g.moe_expert_gemv(g.Q4_K, wg_, wu_, wd_, e, h, f, x, ii, pp, y, ws)
+            def layer(c):
+                def run():
+                    wg_, wu_, wd_ = sets[c]
+                    ii, pp, _ = g.moe_route(wr, x, k)
+                    g.moe_expert_gemv(g.Q4_K, wg_, wu_, wd_, e, h, f, x, ii, pp, y, ws)
+                return run
 
-            for i in range(10):
-                step(i)
-            ms = _events_time(torch, step, 100)
+            graphs = capture(torch, [layer(c) for c in range(copies)])
+            ms = replay_ms(torch, graphs, 50 * copies)
             gbs = alg / (ms * 1e-3) / 1e9
             res[f"t{t}"] = {"us": round(ms * 1e3, 3), "distinct_experts": distinct,
                             "alg_bytes": alg, "GB/s": round(gbs, 1),
                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-            del sets
+            del graphs, sets
         out["moe_q4k"] = res
     if only in (None, "gemm"):
         res = {}
@@ -270,21 +283,20 @@ def secondary(g, torch, synth, only=None):
             c = torch.empty((m, n), dtype=torch.float32, device=dev)
             ws = torch.empty(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
                              device=dev)
-            f = lambda i: g.quant_gemm(fmt, w, n, k, a, c, ws)
-            for i in range(5):
-                f(i)
-            ms = _events_time(torch, f, 30)
+            graphs = capture(torch, [lambda: g.quant_gemm(fmt, w, n, k, a, c, ws)])
+            ms = replay_ms(torch, graphs, 30)
             tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
             res[name] = {"shape": f"{m}x{n}x{k}", "us": round(ms * 1e3, 2),
                          "TFLOP/s": round(tflops, 1),
                          "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+            del graphs
         out["pp512_gemm"] = res
     return out
 
 
 def cpu_baseline(synth, shapes, seconds):
     """The oracle (fp64 C loops) on the same layer set, batch 1 then batch 8,
-    repeated until `seconds` of CPU time have passed (at least one full pass)."""
+    repeated until `seconds` have passed (at least one full pass)."""
     import oracle
 
     threads = oracle.default_threads()

@@ -94,6 +94,29 @@ int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, in
                float *y, int64_t ldy, int batch, void *stream);
 
 /*
+ * quant_gemv_grouped -- several decode products of the same format and batch in
+ * one launch: for each descriptor i,
+ *     descs[i].y[b][r] = sum_c descs[i].w[r][c] * descs[i].x[b][c]
+ * with the same rules and tolerance as quant_gemv.  Meant for the projections of
+ * a decoder layer (README "Components": kernel fusion), so that small matrices
+ * share one launch instead of each paying its own start-up.  The descriptor
+ * array is read on the host during the call and may be reused afterwards.
+ *   count  1..16;  descriptors with n == 0 are skipped
+ * Errors: as quant_gemv, for any descriptor; nothing is launched on error.
+ */
+typedef struct ggq_gemv_desc {
+    const void *w;     /* N x K quantized matrix, 16-byte aligned */
+    int64_t n;
+    int64_t k;
+    const float *x;    /* [batch][ldx], 16-byte aligned, ldx % 4 == 0, ldx >= k */
+    int64_t ldx;
+    float *y;          /* [batch][ldy], ldy >= n */
+    int64_t ldy;
+} ggq_gemv_desc;
+
+int quant_gemv_grouped(int type, const ggq_gemv_desc *descs, int count, int batch, void *stream);
+
+/*
  * quant_gemm_workspace_size -- bytes of device workspace quant_gemm needs for
  * these sizes (the bf16 copy of A plus tile bookkeeping).  0 on bad arguments.
  */

@@ -44,6 +44,7 @@ _SIGS = {
     "ggq_version": (_I, []),
     "quant_dequantize": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "quant_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _P]),
+    "quant_gemv_grouped": (_I, [_I, _P, _I, _I, _P]),
     "quant_gemm_workspace_size": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "quant_gemm": (_I, [_I, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I, _P, _SZ, _P]),
     "moe_route": (_I, [_P, _I64, _I64, _P, _I64, _I, _P, _P, _P, _P]),
@@ -134,6 +135,74 @@ def quant_gemv(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
     _dev(y, "y", torch.float32)
     _ck("quant_gemv", _lib.quant_gemv(fmt, _ptr(w), n, k, _ptr(x2), k, _ptr(y), n, b, _stream()))
     return y[0] if squeeze else y
+
+
+class GemvDesc(ctypes.Structure):
+    """Mirror of ggq_gemv_desc."""
+    _fields_ = [("w", _P), ("n", _I64), ("k", _I64), ("x", _P), ("ldx", _I64), ("y", _P),
+                ("ldy", _I64)]
+
+
+MAX_GROUP = 16
+
+
+def quant_gemv_grouped(fmt: int, items, batch: int | None = None):
+    """One launch for several products of the same format and batch.
+
+    items: sequence of (w, n, k, x, y) with x [B, K] and y [B, N] device tensors.
+    Returns the list of y tensors."""
+    items = list(items)
+    if not 1 <= len(items) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} matrices per grouped call")
+    arr = (GemvDesc * len(items))()
+    b = None
+    for i, (w, n, k, x, y) in enumerate(items):
+        _wbytes(w, fmt, n, k)
+        _dev(x, "x", torch.float32)
+        _dev(y, "y", torch.float32)
+        if x.dim() != 2 or y.dim() != 2 or x.shape[1] != k or y.shape[1] != n or x.shape[0] != y.shape[0]:
+            raise ValueError("x must be [B, K] and y [B, N]")
+        if b is None:
+            b = x.shape[0]
+        elif b != x.shape[0]:
+            raise ValueError("every matrix of a group must have the same batch")
+        arr[i] = GemvDesc(_ptr(w), n, k, _ptr(x), k, _ptr(y), n)
+    _ck("quant_gemv_grouped", _lib.quant_gemv_grouped(fmt, ctypes.cast(arr, _P), len(items),
+                                                      batch or b, _stream()))
+    return [it[4] for it in items]
+
+
+class GemvGroup:
+    """A grouped call whose arguments are validated and marshalled once; calling
+    the object launches it on the current stream.  For decode loops that issue
+    the same products every token (and for graph capture)."""
+
+    def __init__(self, fmt: int, items):
+        items = list(items)
+        if not 1 <= len(items) <= MAX_GROUP:
+            raise ValueError(f"1..{MAX_GROUP} matrices per grouped call")
+        self.fmt = fmt
+        self._keep = items
+        self._arr = (GemvDesc * len(items))()
+        self.batch = None
+        for i, (w, n, k, x, y) in enumerate(items):
+            _wbytes(w, fmt, n, k)
+            _dev(x, "x", torch.float32)
+            _dev(y, "y", torch.float32)
+            if x.dim() != 2 or y.dim() != 2 or x.shape[1] != k or y.shape[1] != n:
+                raise ValueError("x must be [B, K] and y [B, N]")
+            if self.batch is None:
+                self.batch = x.shape[0]
+            elif self.batch != x.shape[0] or y.shape[0] != x.shape[0]:
+                raise ValueError("every matrix of a group must have the same batch")
+            self._arr[i] = GemvDesc(_ptr(w), n, k, _ptr(x), k, _ptr(y), n)
+        self._ptr = ctypes.cast(self._arr, _P)
+        self.count = len(items)
+        self.weight_bytes = sum(n * row_bytes(fmt, k) for _, n, k, _, _ in items)
+
+    def __call__(self):
+        _ck("quant_gemv_grouped", _lib.quant_gemv_grouped(self.fmt, self._ptr, self.count,
+                                                          self.batch, _stream()))
 
 
 def quant_gemm_workspace_size(fmt: int, m: int, n: int, k: int, mode: int = GEMM_BF16) -> int:

@@ -50,19 +50,44 @@ int quant_dequantize(int type, const void* w, int64_t n, int64_t k, float* out, 
                                         as_stream(stream)));
 }
 
-int quant_gemv(int type, const void* w, int64_t n, int64_t k, const float* x, int64_t ldx,
-               float* y, int64_t ldy, int batch, void* stream) {
+namespace {
+// Validation shared by quant_gemv and quant_gemv_grouped.  Tiles are counted in
+// int32 inside the kernels: N is capped at 2^31 rows.
+int check_gemv(int type, const ggq_gemv_desc& d, int batch) {
     const int blk = block_of(type);
     if (!blk) return GGQ_ERR_UNSUPPORTED;
-    if (n < 0 || k <= 0 || k % blk != 0 || k > INT_MAX || n > (int64_t)INT_MAX * 8)
+    if (d.n < 0 || d.k <= 0 || d.k % blk != 0 || d.k > INT_MAX || d.n > INT_MAX)
         return GGQ_ERR_ARG;
     if (batch < 1 || batch > kMaxBatch) return GGQ_ERR_ARG;
-    if (ldx < k || ldy < n) return GGQ_ERR_ARG;
-    if (n == 0) return GGQ_OK;
-    if (!w || !x || !y) return GGQ_ERR_ARG;
-    if (!aligned(w, 16) || !aligned(x, 16) || ldx % 4 != 0 || !aligned(y, 4)) return GGQ_ERR_ALIGN;
-    return launched(ggq::launch_gemv(type, static_cast<const uint8_t*>(w), n, k, x, ldx, y, ldy,
-                                     batch, as_stream(stream)));
+    if (d.ldx < d.k || d.ldy < d.n) return GGQ_ERR_ARG;
+    if (d.n == 0) return GGQ_OK;
+    if (!d.w || !d.x || !d.y) return GGQ_ERR_ARG;
+    if (!aligned(d.w, 16) || !aligned(d.x, 16) || d.ldx % 4 != 0 || !aligned(d.y, 4))
+        return GGQ_ERR_ALIGN;
+    return GGQ_OK;
+}
+}  // namespace
+
+int quant_gemv(int type, const void* w, int64_t n, int64_t k, const float* x, int64_t ldx,
+               float* y, int64_t ldy, int batch, void* stream) {
+    const ggq_gemv_desc d{w, n, k, x, ldx, y, ldy};
+    const int st = check_gemv(type, d, batch);
+    if (st != GGQ_OK || n == 0) return st;
+    return launched(ggq::launch_gemv_group(type, &d, 1, batch, as_stream(stream)));
+}
+
+int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batch,
+                       void* stream) {
+    if (!block_of(type)) return GGQ_ERR_UNSUPPORTED;
+    if (!descs || count < 1 || count > ggq::gemv_max_group()) return GGQ_ERR_ARG;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        const int st = check_gemv(type, descs[i], batch);
+        if (st != GGQ_OK) return st;
+        tiles += (descs[i].n + 7) / 8;
+    }
+    if (tiles > INT_MAX) return GGQ_ERR_ARG;
+    return launched(ggq::launch_gemv_group(type, descs, count, batch, as_stream(stream)));
 }
 
 size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int mode) {

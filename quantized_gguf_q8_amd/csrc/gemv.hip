@@ -1,6 +1,27 @@
-// gemv.hip -- quant_gemv: decode-time matrix-vector product over Q8_0 / Q4_K rows,
-// batch 1..16, weights decoded on the fly and never written back (Phobos README,
-// "Inference").  The workgroup algorithm is in gemv_core.h.
+// gemv.hip -- quant_gemv / quant_gemv_grouped: decode-time matrix-vector products
+// over Q8_0 / Q4_K rows, batch 1..16, weights decoded on the fly and never
+// written back (Phobos README, "Inference").  A grouped call runs several
+// matrices (e.g. every projection of a decoder layer, README "Components":
+// kernel fusion) in one launch.
+//
+// Streaming structure (gfx950, 256-thread workgroups, wave64):
+//  * Work unit = (matrix, tile of ROWS rows, K chunk of KC = 64*SL weights),
+//    SL = 256/ROWS.  Thread (row rl, slice s), slice fastest, owns 64 weights of
+//    its row per chunk: two Q8_0 blocks or a 64-weight quarter of a Q4_K
+//    super-block.
+//  * Workgroups are persistent: each walks its share of the unit stream.  While
+//    it computes unit u from one LDS buffer, the 16-byte global loads of unit
+//    u+1 (weights, coalesced along each row, and the activation chunk) are
+//    already in flight into registers; they land in the other LDS buffer after
+//    the compute, so one barrier per unit suffices and HBM never waits for the
+//    arithmetic.
+//  * A thread decodes its 64 weights once and applies them to every batch row.
+//  * The SL slices of a row sit in one wave (slice fastest, SL divides 64), so
+//    a row's partials are combined with a fixed butterfly of lane shuffles:
+//    deterministic, no LDS round trip.
+//  * Q4_K uses the factored form per 32-weight sub-block j,
+//        d*sc_j * sum q_c x_c - dmin*m_j * sum x_c,
+//    with the activation sums formed once per chunk while staging.
 #include "gemv_core.h"
 #include "ggq_launch.h"
 
@@ -8,26 +29,226 @@ namespace ggq {
 
 namespace {
 
-struct StoreEpi {
+constexpr int kMaxJobs = 16;
+
+struct GemvJob {
+    const uint8_t* w;
+    const float* x;
     float* y;
+    int64_t n;
+    int64_t ldx;
     int64_t ldy;
-    __device__ void operator()(int b, int64_t r, const float (&v)[1]) const {
-        y[(int64_t)b * ldy + r] = v[0];
+    int64_t rb;      // bytes per row
+    int32_t k;
+    int32_t nchunk;  // K chunks per tile
+    int32_t tile0;   // first tile of this job in the grouped tile index space
+    int32_t tiles;
+};
+
+struct GemvJobs {
+    GemvJob j[kMaxJobs];
+    int32_t count;
+    int32_t total_tiles;
+};
+
+template <int FMT, int NB, int ROWS>
+struct StreamCfg {
+    using Base = GemvCfg<FMT, NB, ROWS, 1>;
+    static constexpr int SL = Base::SL;
+    static constexpr int KC = Base::KC;
+    static constexpr int CRB = Base::CRB;
+    static constexpr int WRS = Base::WRS;
+    static constexpr int XSS = Base::XSS;
+    static constexpr int XBS = Base::XBS;
+    static constexpr int PPR = CRB / 16;               // 16-byte pieces per row chunk
+    static constexpr int WPIECES = ROWS * PPR;
+    static constexpr int WP = (WPIECES + 255) / 256;   // per thread
+    static constexpr int XPIECES = NB * KC / 4;        // float4 pieces of the x chunk
+    static constexpr int XP = (XPIECES + 255) / 256;
+    static constexpr int kWBytes = ROWS * WRS;
+    static constexpr int kXBytes = NB * XBS * 4;
+    static constexpr int kSumBytes = FMT == kQ4_K ? NB * SL * 2 * 4 : 0;
+    static constexpr int kBuf = kWBytes + kXBytes + kSumBytes;
+    static constexpr int kLds = 2 * kBuf;
+};
+
+// A unit is one K chunk of one tile.  A workgroup takes tiles bid, bid+G, ...
+// and walks each tile's chunks in order, so a row's partial sums stay in the
+// registers of the threads that own it.
+struct UnitPos {
+    int tile;   // grouped tile index
+    int job;
+    int64_t r0;
+    int chunk;
+};
+
+__device__ __forceinline__ UnitPos locate(const GemvJobs& jobs, int tile, int chunk, int rows) {
+    int j = 0;
+    while (j + 1 < jobs.count && tile >= jobs.j[j + 1].tile0) ++j;
+    UnitPos p;
+    p.tile = tile;
+    p.job = j;
+    p.r0 = (int64_t)(tile - jobs.j[j].tile0) * rows;
+    p.chunk = chunk;
+    return p;
+}
+
+template <int FMT, int NB, int ROWS>
+struct Prefetch {
+    using C = StreamCfg<FMT, NB, ROWS>;
+    uint4 w[C::WP];
+    float4 x[C::XP];
+
+    __device__ __forceinline__ void load(const GemvJobs& jobs, const UnitPos& p, int batch,
+                                         int tid) {
+        const GemvJob& jb = jobs.j[p.job];
+        const int64_t cb0 = (int64_t)p.chunk * C::CRB;
+#pragma unroll
+        for (int i = 0; i < C::WP; ++i) {
+            const int q = tid + 256 * i;
+            const int pr = q / C::PPR;
+            const int off = (q % C::PPR) * 16;
+            w[i] = make_uint4(0, 0, 0, 0);
+            if (q < C::WPIECES && p.r0 + pr < jb.n && cb0 + off < jb.rb)
+                w[i] = load_once16(jb.w + (p.r0 + pr) * jb.rb + cb0 + off);
+        }
+        const int k0 = p.chunk * C::KC;
+#pragma unroll
+        for (int i = 0; i < C::XP; ++i) {
+            const int q = tid + 256 * i;
+            const int b = q / (C::KC / 4);
+            const int pos = (q % (C::KC / 4)) * 4;
+            x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (q < C::XPIECES && b < batch && k0 + pos < jb.k)
+                x[i] = *reinterpret_cast<const float4*>(jb.x + b * jb.ldx + k0 + pos);
+        }
+    }
+
+    __device__ __forceinline__ void store(uint8_t* buf, int tid) const {
+        uint8_t* lw = buf;
+        float* lx = reinterpret_cast<float*>(buf + C::kWBytes);
+        float* lsum = reinterpret_cast<float*>(buf + C::kWBytes + C::kXBytes);
+#pragma unroll
+        for (int i = 0; i < C::WP; ++i) {
+            const int q = tid + 256 * i;
+            if (q < C::WPIECES) {
+                const int pr = q / C::PPR;
+                const int off = (q % C::PPR) * 16;
+                *reinterpret_cast<uint4*>(lw + pr * C::WRS + off) = w[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::XP; ++i) {
+            const int q = tid + 256 * i;
+            if (C::XPIECES % 256 == 0 || q < C::XPIECES) {  // whole waves only
+                const int b = q / (C::KC / 4);
+                const int pos = (q % (C::KC / 4)) * 4;
+                const float4 v = x[i];
+                *reinterpret_cast<float4*>(lx + b * C::XBS + (pos >> 6) * C::XSS + (pos & 63)) = v;
+                if constexpr (FMT == kQ4_K) {
+                    float t = (v.x + v.y) + (v.z + v.w);
+                    t += __shfl_xor(t, 1, 64);
+                    t += __shfl_xor(t, 2, 64);
+                    t += __shfl_xor(t, 4, 64);
+                    if ((q & 7) == 0) lsum[(b * C::SL + (pos >> 6)) * 2 + ((pos >> 5) & 1)] = t;
+                }
+            }
+        }
     }
 };
 
 template <int FMT, int NB, int ROWS>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ w, int64_t n, int k,
-                                                   int64_t rbytes, const float* __restrict__ x,
-                                                   int64_t ldx, float* __restrict__ y,
-                                                   int64_t ldy, int batch) {
+__global__ __launch_bounds__(256) void gemv_stream_kernel(const GemvJobs jobs, int batch) {
+    using C = StreamCfg<FMT, NB, ROWS>;
+    constexpr int SL = C::SL;
     extern __shared__ __align__(16) uint8_t lds[];
-    const uint8_t* wm[1] = {w};
-    const float* xr[NB];
+    const int tid = threadIdx.x;
+    const int s = tid % SL;
+    const int rl = tid / SL;
+
+    if ((int)blockIdx.x >= jobs.total_tiles) return;
+    Prefetch<FMT, NB, ROWS> pf;
+    UnitPos cur = locate(jobs, blockIdx.x, 0, ROWS);
+    pf.load(jobs, cur, batch, tid);
+    pf.store(lds, tid);
+    __syncthreads();
+
+    float acc[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) xr[b] = x + (int64_t)b * ldx;
-    StoreEpi epi{y, ldy};
-    gemv_tile<FMT, NB, ROWS, 1>(lds, wm, n, k, rbytes, xr, batch, (int64_t)blockIdx.x * ROWS, epi);
+    for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+
+    int buf = 0;
+    for (;;) {
+        UnitPos nxt;
+        bool more;
+        if (cur.chunk + 1 < jobs.j[cur.job].nchunk) {
+            more = true;
+            nxt = cur;
+            nxt.chunk = cur.chunk + 1;
+        } else {
+            const int tn = cur.tile + (int)gridDim.x;
+            more = tn < jobs.total_tiles;
+            if (more) nxt = locate(jobs, tn, 0, ROWS);
+        }
+        if (more) pf.load(jobs, nxt, batch, tid);
+        // ---- compute unit u from LDS buffer `buf` ----
+        {
+            const GemvJob& jb = jobs.j[cur.job];
+            const uint8_t* base = lds + buf * C::kBuf;
+            const uint8_t* lw = base;
+            const float* lx = reinterpret_cast<const float*>(base + C::kWBytes);
+            const float* lsum = reinterpret_cast<const float*>(base + C::kWBytes + C::kXBytes);
+            const int k0 = cur.chunk * C::KC;
+            if (cur.r0 + rl < jb.n && k0 + s * 64 < jb.k) {
+                float f0[32], f1[32];
+                float sa0, sa1, mb0, mb1;
+                decode_unit<FMT>(lw + rl * C::WRS, s, f0, f1, sa0, sa1, mb0, mb1);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b < batch) {
+                        const float4* xv = reinterpret_cast<const float4*>(lx + b * C::XBS + s * C::XSS);
+                        float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            float4 a = xv[i];
+                            float4 e = xv[8 + i];
+                            p0[i & 3] += f0[4 * i] * a.x + f0[4 * i + 1] * a.y +
+                                         f0[4 * i + 2] * a.z + f0[4 * i + 3] * a.w;
+                            p1[i & 3] += f1[4 * i] * e.x + f1[4 * i + 1] * e.y +
+                                         f1[4 * i + 2] * e.z + f1[4 * i + 3] * e.w;
+                        }
+                        float t = sa0 * ((p0[0] + p0[1]) + (p0[2] + p0[3])) +
+                                  sa1 * ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+                        if constexpr (FMT == kQ4_K) {
+                            const float* xs = lsum + (b * SL + s) * 2;
+                            t -= mb0 * xs[0] + mb1 * xs[1];
+                        }
+                        acc[b] += t;
+                    }
+                }
+            }
+            if (cur.chunk == jb.nchunk - 1) {
+                // row finished: butterfly over the SL slice lanes of this row
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                    for (int o = 1; o < SL; o <<= 1) acc[b] += __shfl_xor(acc[b], o, 64);
+                }
+                if (s == 0 && cur.r0 + rl < jb.n) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        if (b < batch) jb.y[b * jb.ldy + cur.r0 + rl] = acc[b];
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+            }
+        }
+        if (!more) break;
+        buf ^= 1;
+        pf.store(lds + buf * C::kBuf, tid);
+        __syncthreads();
+        cur = nxt;
+    }
 }
 
 // Fallback for Q8_0 rows that are not whole 16-byte pieces (K % 256 != 0): one
@@ -73,44 +294,74 @@ __global__ __launch_bounds__(64) void gemv_q8_0_generic(const uint8_t* __restric
     }
 }
 
+int device_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
 template <int FMT, int NB, int ROWS>
-hipError_t launch_cfg(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const float* x,
-                      int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s) {
-    using C = GemvCfg<FMT, NB, ROWS, 1>;
-    dim3 grid((unsigned)((n + ROWS - 1) / ROWS));
-    hipLaunchKernelGGL((gemv_kernel<FMT, NB, ROWS>), grid, dim3(256), C::kLds, s, w, n, (int)k, rb,
-                       x, ldx, y, ldy, batch);
+hipError_t launch_stream(GemvJobs& jobs, int batch, hipStream_t s) {
+    using C = StreamCfg<FMT, NB, ROWS>;
+    static int per_cu = 0;
+    if (!per_cu) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gemv_stream_kernel<FMT, NB, ROWS>, 256,
+                                                         C::kLds) != hipSuccess || v <= 0)
+            v = 2;
+        per_cu = v;
+    }
+    int total = 0;
+    for (int i = 0; i < jobs.count; ++i) {
+        GemvJob& jb = jobs.j[i];
+        const int64_t tiles = (jb.n + ROWS - 1) / ROWS;
+        jb.nchunk = (jb.k + C::KC - 1) / C::KC;
+        jb.tile0 = total;
+        jb.tiles = (int32_t)tiles;
+        total += jb.tiles;
+    }
+    jobs.total_tiles = total;
+    if (total == 0) return hipSuccess;
+    const int64_t slots = (int64_t)per_cu * device_cus();
+    const unsigned grid = (unsigned)(total < slots ? total : slots);
+    hipLaunchKernelGGL((gemv_stream_kernel<FMT, NB, ROWS>), dim3(grid), dim3(256), C::kLds, s, jobs,
+                       batch);
     return hipGetLastError();
 }
 
 template <int FMT, int NB>
-hipError_t launch_nb(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const float* x,
-                     int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s) {
-    const int rows = gemv_rows_for(NB, k);
+hipError_t launch_nb(GemvJobs& jobs, int batch, int64_t kmin, hipStream_t s) {
+    const int rows = gemv_rows_for(NB, kmin);
     if constexpr (2 * NB <= 8)
-        if (rows == 8) return launch_cfg<FMT, NB, 8>(w, n, k, rb, x, ldx, y, ldy, batch, s);
+        if (rows == 8) return launch_stream<FMT, NB, 8>(jobs, batch, s);
     if constexpr (2 * NB <= 16)
-        if (rows == 16) return launch_cfg<FMT, NB, 16>(w, n, k, rb, x, ldx, y, ldy, batch, s);
+        if (rows == 16) return launch_stream<FMT, NB, 16>(jobs, batch, s);
     if constexpr (2 * NB <= 32)
-        if (rows == 32) return launch_cfg<FMT, NB, 32>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    return launch_cfg<FMT, NB, 64>(w, n, k, rb, x, ldx, y, ldy, batch, s);
+        if (rows == 32) return launch_stream<FMT, NB, 32>(jobs, batch, s);
+    return launch_stream<FMT, NB, 64>(jobs, batch, s);
 }
 
 template <int FMT>
-hipError_t launch_fmt(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const float* x,
-                      int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s) {
-    if (batch <= 1) return launch_nb<FMT, 1>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    if (batch <= 2) return launch_nb<FMT, 2>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    if (batch <= 4) return launch_nb<FMT, 4>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    if (batch <= 8) return launch_nb<FMT, 8>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    return launch_nb<FMT, 16>(w, n, k, rb, x, ldx, y, ldy, batch, s);
+hipError_t launch_fmt(GemvJobs& jobs, int batch, int64_t kmin, hipStream_t s) {
+    if (batch <= 1) return launch_nb<FMT, 1>(jobs, batch, kmin, s);
+    if (batch <= 2) return launch_nb<FMT, 2>(jobs, batch, kmin, s);
+    if (batch <= 4) return launch_nb<FMT, 4>(jobs, batch, kmin, s);
+    if (batch <= 8) return launch_nb<FMT, 8>(jobs, batch, kmin, s);
+    return launch_nb<FMT, 16>(jobs, batch, kmin, s);
 }
 
 template <int NB>
-hipError_t launch_generic(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const float* x,
-                          int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s) {
-    hipLaunchKernelGGL((gemv_q8_0_generic<NB>), dim3((unsigned)n), dim3(64), 0, s, w, (int)k, rb,
-                       x, ldx, y, ldy, batch);
+hipError_t launch_generic(const GemvDesc& d, int batch, hipStream_t s) {
+    const int64_t rb = row_bytes(kQ8_0, d.k);
+    hipLaunchKernelGGL((gemv_q8_0_generic<NB>), dim3((unsigned)d.n), dim3(64), 0, s,
+                       static_cast<const uint8_t*>(d.w), (int)d.k, rb, d.x, d.ldx, d.y, d.ldy,
+                       batch);
     return hipGetLastError();
 }
 
@@ -120,13 +371,40 @@ int64_t row_bytes(int type, int64_t k) {
     return type == kQ8_0 ? k / 32 * kQ8Bytes : k / 256 * kQ4Bytes;
 }
 
+int gemv_max_group() { return kMaxJobs; }
+
+hipError_t launch_gemv_group(int type, const GemvDesc* descs, int count, int batch,
+                             hipStream_t s) {
+    GemvJobs jobs{};
+    int64_t kmin = INT64_MAX;
+    for (int i = 0; i < count; ++i) {
+        const GemvDesc& d = descs[i];
+        if (d.n == 0) continue;
+        if (type == kQ8_0 && d.k % 256 != 0) {
+            hipError_t e = batch <= 4 ? launch_generic<4>(d, batch, s) : launch_generic<16>(d, batch, s);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        GemvJob& jb = jobs.j[jobs.count++];
+        jb.w = static_cast<const uint8_t*>(d.w);
+        jb.x = d.x;
+        jb.y = d.y;
+        jb.n = d.n;
+        jb.ldx = d.ldx;
+        jb.ldy = d.ldy;
+        jb.rb = row_bytes(type, d.k);
+        jb.k = (int32_t)d.k;
+        if (d.k < kmin) kmin = d.k;
+    }
+    if (jobs.count == 0) return hipSuccess;
+    if (type == kQ4_K) return launch_fmt<kQ4_K>(jobs, batch, kmin, s);
+    return launch_fmt<kQ8_0>(jobs, batch, kmin, s);
+}
+
 hipError_t launch_gemv(int type, const uint8_t* w, int64_t n, int64_t k, const float* x,
                        int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s) {
-    const int64_t rb = row_bytes(type, k);
-    if (type == kQ4_K) return launch_fmt<kQ4_K>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    if (k % 256 == 0) return launch_fmt<kQ8_0>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    if (batch <= 4) return launch_generic<4>(w, n, k, rb, x, ldx, y, ldy, batch, s);
-    return launch_generic<16>(w, n, k, rb, x, ldx, y, ldy, batch, s);
+    GemvDesc d{w, n, k, x, ldx, y, ldy};
+    return launch_gemv_group(type, &d, 1, batch, s);
 }
 
 }  // namespace ggq

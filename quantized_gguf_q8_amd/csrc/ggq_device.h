@@ -81,6 +81,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data that is read exactly once (weights): non-temporal, so it
+// does not evict the activations and partial results from the caches.
+__device__ __forceinline__ uint4 load_once16(const void* p) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -6,13 +6,19 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ggq.h"
+
 namespace ggq {
+
+using GemvDesc = ggq_gemv_desc;
 
 int64_t row_bytes(int type, int64_t k);
 
 hipError_t launch_dequant(int type, const uint8_t* w, int64_t n, int64_t k, float* out,
                           hipStream_t s);
 
+int gemv_max_group();
+hipError_t launch_gemv_group(int type, const GemvDesc* descs, int count, int batch, hipStream_t s);
 hipError_t launch_gemv(int type, const uint8_t* w, int64_t n, int64_t k, const float* x,
                        int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s);
 
