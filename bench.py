@@ -115,10 +115,12 @@ def main():
                 synth.normal_f32((b, k), seed=0, tensor_id=synth.tid(1, n, k) + b)).to(dev)
             ys[(name, b)] = torch.empty((b, n), dtype=torch.float32, device=dev)
     groups = []   # per copy: (batch-1 group, batch-8 group)
-    for ws in dev_sets:
+    for wset in dev_sets:
+        # batch 1: vector units, no workspace; batch 8: matrix cores with a workspace
         groups.append(tuple(
             g.GemvGroup(g.Q8_0, [(w, n, k, xs[(name, b)], ys[(name, b)])
-                                 for (name, n, k), w in zip(shapes, ws)]) for b in (1, 8)))
+                                 for (name, n, k), w in zip(shapes, wset)],
+                        ws=None if b == 1 else "auto") for b in (1, 8)))
     torch.cuda.synchronize()
     weight_bytes_step = 2 * set_bytes
 
@@ -186,7 +188,8 @@ def main():
         "config": {
             "workload": "dense ~1B decode layer set, Q8_0 weights: qkv 3072x2048, o 2048x2048, "
                         "gate 6144x2048, up 6144x2048, down 2048x6144, head 65536x2048; "
-                        "batch 1 then batch 8 per step, one grouped launch per batch",
+                        "batch 1 then batch 8 per step, one grouped launch per batch "
+                        "(batch 8 on the matrix cores)",
             "weight_format": "q8_0",
             "weight_bytes_per_step": weight_bytes_step,
             "weight_copies_cycled": copies,
@@ -228,7 +231,8 @@ def secondary(g, torch, synth, only=None):
             for b in (1, 4, 16):
                 x = torch.from_numpy(synth.normal_f32((b, k), 0, synth.tid(2, n, k) + 1)).to(dev)
                 y = torch.empty((b, n), dtype=torch.float32, device=dev)
-                calls = [g.GemvGroup(g.Q4_K, [(c, n, k, x, y)]) for c in cps]
+                calls = [g.GemvGroup(g.Q4_K, [(c, n, k, x, y)], ws=None if b == 1 else "auto")
+                         for c in cps]
                 per = 16
                 fns = [(lambda j0: (lambda: [calls[(j0 + j) % copies]() for j in range(per)]))(j0)
                        for j0 in range(0, copies, per)]

@@ -82,16 +82,29 @@ int quant_dequantize(int type, const void *w, int64_t n, int64_t k, float *out, 
  *     y[b][r] = sum_c w[r][c] * x[b][c]   for b < batch, r < N
  * with the weights decoded on the fly (never materialised) and one read of W
  * serving every batch row (README "Inference": the decode-time product).
- * fp32 arithmetic; the result is within 1e-5 * sum_c |w x| of the exact value.
+ * The result is within 1e-5 * sum_c |w x| of the exact value.
  *   w     device, 16-byte aligned
  *   x     device fp32 [batch][ldx], ldx >= K, 16-byte aligned, ldx % 4 == 0
  *   y     device fp32 [batch][ldy], ldy >= N
  *   batch 1..16
+ *   ws    NULL, or device workspace of at least quant_gemv_workspace_size(type, K,
+ *         batch) bytes, 256-byte aligned, not shared with a call running at the
+ *         same time.  With a workspace and batch >= 2 the activations are split
+ *         into exact fp16 pairs once and the products run on the matrix cores
+ *         (fp32 accumulation); with NULL every batch row costs one fp32 FMA per
+ *         weight on the vector units.  Both meet the same tolerance.
+ * A matrix may hold at most 4 GiB ((N + 64) * row bytes < 2^32) and an activation
+ * block batch * ldx * 4 < 2^32 bytes.
  * N == 0 is a no-op.  Errors: GGQ_ERR_ARG (null, K not a multiple of the block,
- * batch out of range, ld too small), GGQ_ERR_ALIGN, GGQ_ERR_UNSUPPORTED.
+ * batch out of range, ld too small, size limits), GGQ_ERR_ALIGN, GGQ_ERR_WORKSPACE
+ * (ws given but too small), GGQ_ERR_UNSUPPORTED.
  */
 int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t ldx,
-               float *y, int64_t ldy, int batch, void *stream);
+               float *y, int64_t ldy, int batch, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes one matrix of K columns needs in quant_gemv (and in each
+ * descriptor of quant_gemv_grouped) at this batch; 0 on bad arguments. */
+size_t quant_gemv_workspace_size(int type, int64_t k, int batch);
 
 /*
  * quant_gemv_grouped -- several decode products of the same format and batch in
@@ -102,6 +115,8 @@ int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, in
  * share one launch instead of each paying its own start-up.  The descriptor
  * array is read on the host during the call and may be reused afterwards.
  *   count  1..16;  descriptors with n == 0 are skipped
+ *   ws     NULL, or at least the sum over descriptors of
+ *          quant_gemv_workspace_size(type, descs[i].k, batch) bytes
  * Errors: as quant_gemv, for any descriptor; nothing is launched on error.
  */
 typedef struct ggq_gemv_desc {
@@ -114,7 +129,8 @@ typedef struct ggq_gemv_desc {
     int64_t ldy;
 } ggq_gemv_desc;
 
-int quant_gemv_grouped(int type, const ggq_gemv_desc *descs, int count, int batch, void *stream);
+int quant_gemv_grouped(int type, const ggq_gemv_desc *descs, int count, int batch, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /*
  * quant_gemm_workspace_size -- bytes of device workspace quant_gemm needs for

@@ -43,8 +43,9 @@ _SIGS = {
     "ggq_status_string": (ctypes.c_char_p, [_I]),
     "ggq_version": (_I, []),
     "quant_dequantize": (_I, [_I, _P, _I64, _I64, _P, _P]),
-    "quant_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _P]),
-    "quant_gemv_grouped": (_I, [_I, _P, _I, _I, _P]),
+    "quant_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _P, _SZ, _P]),
+    "quant_gemv_workspace_size": (_SZ, [_I, _I64, _I]),
+    "quant_gemv_grouped": (_I, [_I, _P, _I, _I, _P, _SZ, _P]),
     "quant_gemm_workspace_size": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "quant_gemm": (_I, [_I, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I, _P, _SZ, _P]),
     "moe_route": (_I, [_P, _I64, _I64, _P, _I64, _I, _P, _P, _P, _P]),
@@ -120,9 +121,28 @@ def quant_dequantize(fmt: int, w: torch.Tensor, n: int, k: int,
     return out
 
 
+def quant_gemv_workspace_size(fmt: int, k: int, batch: int) -> int:
+    return _lib.quant_gemv_workspace_size(fmt, k, batch)
+
+
+def _ws_arg(ws, need, device):
+    """None -> no workspace (vector-unit path); "auto" -> allocate; else a uint8 tensor."""
+    if ws is None:
+        return None
+    if isinstance(ws, str):
+        if ws != "auto":
+            raise ValueError("ws must be None, 'auto' or a uint8 device tensor")
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    _dev(ws, "ws", torch.uint8)
+    return ws
+
+
 def quant_gemv(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
-               y: torch.Tensor | None = None) -> torch.Tensor:
-    """y[b][r] = sum_c w[r][c] x[b][c]; x is [B, K] (B <= 16) or [K]."""
+               y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
+    """y[b][r] = sum_c w[r][c] x[b][c]; x is [B, K] (B <= 16) or [K].
+
+    ws=None runs the fp32 vector-unit kernel; a workspace ("auto" or a uint8
+    tensor of quant_gemv_workspace_size bytes) lets batch >= 2 use the matrix cores."""
     _wbytes(w, fmt, n, k)
     squeeze = x.dim() == 1
     x2 = x.unsqueeze(0) if squeeze else x
@@ -133,7 +153,9 @@ def quant_gemv(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
     if y is None:
         y = torch.empty((b, n), dtype=torch.float32, device=w.device)
     _dev(y, "y", torch.float32)
-    _ck("quant_gemv", _lib.quant_gemv(fmt, _ptr(w), n, k, _ptr(x2), k, _ptr(y), n, b, _stream()))
+    wst = _ws_arg(ws, quant_gemv_workspace_size(fmt, k, b), w.device)
+    _ck("quant_gemv", _lib.quant_gemv(fmt, _ptr(w), n, k, _ptr(x2), k, _ptr(y), n, b, _ptr(wst),
+                                      0 if wst is None else wst.numel(), _stream()))
     return y[0] if squeeze else y
 
 
@@ -146,38 +168,13 @@ class GemvDesc(ctypes.Structure):
 MAX_GROUP = 16
 
 
-def quant_gemv_grouped(fmt: int, items, batch: int | None = None):
-    """One launch for several products of the same format and batch.
-
-    items: sequence of (w, n, k, x, y) with x [B, K] and y [B, N] device tensors.
-    Returns the list of y tensors."""
-    items = list(items)
-    if not 1 <= len(items) <= MAX_GROUP:
-        raise ValueError(f"1..{MAX_GROUP} matrices per grouped call")
-    arr = (GemvDesc * len(items))()
-    b = None
-    for i, (w, n, k, x, y) in enumerate(items):
-        _wbytes(w, fmt, n, k)
-        _dev(x, "x", torch.float32)
-        _dev(y, "y", torch.float32)
-        if x.dim() != 2 or y.dim() != 2 or x.shape[1] != k or y.shape[1] != n or x.shape[0] != y.shape[0]:
-            raise ValueError("x must be [B, K] and y [B, N]")
-        if b is None:
-            b = x.shape[0]
-        elif b != x.shape[0]:
-            raise ValueError("every matrix of a group must have the same batch")
-        arr[i] = GemvDesc(_ptr(w), n, k, _ptr(x), k, _ptr(y), n)
-    _ck("quant_gemv_grouped", _lib.quant_gemv_grouped(fmt, ctypes.cast(arr, _P), len(items),
-                                                      batch or b, _stream()))
-    return [it[4] for it in items]
-
-
 class GemvGroup:
     """A grouped call whose arguments are validated and marshalled once; calling
     the object launches it on the current stream.  For decode loops that issue
-    the same products every token (and for graph capture)."""
+    the same products every token (and for graph capture).  items: (w, n, k, x, y)
+    with x [B, K] and y [B, N]; ws as for quant_gemv."""
 
-    def __init__(self, fmt: int, items):
+    def __init__(self, fmt: int, items, ws=None):
         items = list(items)
         if not 1 <= len(items) <= MAX_GROUP:
             raise ValueError(f"1..{MAX_GROUP} matrices per grouped call")
@@ -199,10 +196,22 @@ class GemvGroup:
         self._ptr = ctypes.cast(self._arr, _P)
         self.count = len(items)
         self.weight_bytes = sum(n * row_bytes(fmt, k) for _, n, k, _, _ in items)
+        need = sum(quant_gemv_workspace_size(fmt, k, self.batch) for _, n, k, _, _ in items if n)
+        self.ws = _ws_arg(ws, need, items[0][0].device)
+        self._wsp = _ptr(self.ws)
+        self._wsn = 0 if self.ws is None else self.ws.numel()
 
     def __call__(self):
         _ck("quant_gemv_grouped", _lib.quant_gemv_grouped(self.fmt, self._ptr, self.count,
-                                                          self.batch, _stream()))
+                                                          self.batch, self._wsp, self._wsn,
+                                                          _stream()))
+
+
+def quant_gemv_grouped(fmt: int, items, ws=None):
+    """One launch for several products of the same format and batch; returns the
+    list of y tensors."""
+    GemvGroup(fmt, items, ws)()
+    return [it[4] for it in items]
 
 
 def quant_gemm_workspace_size(fmt: int, m: int, n: int, k: int, mode: int = GEMM_BF16) -> int:

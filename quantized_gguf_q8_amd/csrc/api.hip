@@ -60,6 +60,10 @@ int check_gemv(int type, const ggq_gemv_desc& d, int batch) {
         return GGQ_ERR_ARG;
     if (batch < 1 || batch > kMaxBatch) return GGQ_ERR_ARG;
     if (d.ldx < d.k || d.ldy < d.n) return GGQ_ERR_ARG;
+    // Kernels address a matrix and an activation block with 32-bit buffer offsets.
+    if ((d.n + 64) * ggq::row_bytes(type, d.k) >= ((int64_t)1 << 32) ||
+        (int64_t)batch * d.ldx * 4 >= ((int64_t)1 << 32))
+        return GGQ_ERR_ARG;
     if (d.n == 0) return GGQ_OK;
     if (!d.w || !d.x || !d.y) return GGQ_ERR_ARG;
     if (!aligned(d.w, 16) || !aligned(d.x, 16) || d.ldx % 4 != 0 || !aligned(d.y, 4))
@@ -68,16 +72,49 @@ int check_gemv(int type, const ggq_gemv_desc& d, int batch) {
 }
 }  // namespace
 
+// The matrix-core path needs rows that are whole 16-byte pieces (always true
+// for Q4_K; K % 256 == 0 for Q8_0) and at least two activation rows.
+static bool mfma_ok(int type, const ggq_gemv_desc* d, int count, int batch) {
+    if (batch < 2) return false;
+    for (int i = 0; i < count; ++i)
+        if (d[i].n > 0 && type == GGQ_Q8_0 && d[i].k % 256 != 0) return false;
+    return true;
+}
+
+static size_t gemv_ws_need(int type, const ggq_gemv_desc* d, int count, int batch) {
+    size_t need = 0;
+    for (int i = 0; i < count; ++i)
+        if (d[i].n > 0) need += ggq::gemv_mfma_ws_bytes(type, d[i].k, batch);
+    return need;
+}
+
+static int run_gemv(int type, const ggq_gemv_desc* d, int count, int batch, void* ws,
+                    size_t ws_bytes, void* stream) {
+    if (ws) {
+        if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+        if (ws_bytes < gemv_ws_need(type, d, count, batch)) return GGQ_ERR_WORKSPACE;
+        if (mfma_ok(type, d, count, batch))
+            return launched(ggq::launch_gemv_mfma(type, d, count, batch, ws, as_stream(stream)));
+    }
+    return launched(ggq::launch_gemv_group(type, d, count, batch, as_stream(stream)));
+}
+
 int quant_gemv(int type, const void* w, int64_t n, int64_t k, const float* x, int64_t ldx,
-               float* y, int64_t ldy, int batch, void* stream) {
+               float* y, int64_t ldy, int batch, void* ws, size_t ws_bytes, void* stream) {
     const ggq_gemv_desc d{w, n, k, x, ldx, y, ldy};
     const int st = check_gemv(type, d, batch);
     if (st != GGQ_OK || n == 0) return st;
-    return launched(ggq::launch_gemv_group(type, &d, 1, batch, as_stream(stream)));
+    return run_gemv(type, &d, 1, batch, ws, ws_bytes, stream);
 }
 
-int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batch,
-                       void* stream) {
+size_t quant_gemv_workspace_size(int type, int64_t k, int batch) {
+    const int blk = block_of(type);
+    if (!blk || k <= 0 || k % blk != 0 || batch < 1 || batch > kMaxBatch) return 0;
+    return ggq::gemv_mfma_ws_bytes(type, k, batch);
+}
+
+int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batch, void* ws,
+                       size_t ws_bytes, void* stream) {
     if (!block_of(type)) return GGQ_ERR_UNSUPPORTED;
     if (!descs || count < 1 || count > ggq::gemv_max_group()) return GGQ_ERR_ARG;
     int64_t tiles = 0;
@@ -87,7 +124,8 @@ int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batc
         tiles += (descs[i].n + 7) / 8;
     }
     if (tiles > INT_MAX) return GGQ_ERR_ARG;
-    return launched(ggq::launch_gemv_group(type, descs, count, batch, as_stream(stream)));
+    if (tiles == 0) return GGQ_OK;
+    return run_gemv(type, descs, count, batch, ws, ws_bytes, stream);
 }
 
 size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int mode) {

@@ -68,8 +68,9 @@ struct StreamCfg {
     static constexpr int kWBytes = ROWS * WRS;
     static constexpr int kXBytes = NB * XBS * 4;
     static constexpr int kSumBytes = FMT == kQ4_K ? NB * SL * 2 * 4 : 0;
-    static constexpr int kBuf = kWBytes + kXBytes + kSumBytes;
-    static constexpr int kLds = 2 * kBuf;
+    static constexpr int kXBuf = kXBytes + kSumBytes;
+    // two weight buffers, two activation buffers
+    static constexpr int kLds = 2 * kWBytes + 2 * kXBuf;
 };
 
 // A unit is one K chunk of one tile.  A workgroup takes tiles bid, bid+G, ...
@@ -93,41 +94,58 @@ __device__ __forceinline__ UnitPos locate(const GemvJobs& jobs, int tile, int ch
     return p;
 }
 
+template <int ROWS>
+__device__ __forceinline__ bool next_unit(const GemvJobs& jobs, const UnitPos& p, UnitPos& q) {
+    if (p.chunk + 1 < jobs.j[p.job].nchunk) {
+        q = p;
+        q.chunk = p.chunk + 1;
+        return true;
+    }
+    const int tn = p.tile + (int)gridDim.x;
+    if (tn >= jobs.total_tiles) return false;
+    q = locate(jobs, tn, 0, ROWS);
+    return true;
+}
+
+// Registers holding the next unit's bytes between its global loads and its LDS
+// stores.  Pieces outside the matrix, past a row's end or past K are loaded
+// from an out-of-range buffer offset and come back as zeros.
 template <int FMT, int NB, int ROWS>
 struct Prefetch {
     using C = StreamCfg<FMT, NB, ROWS>;
     uint4 w[C::WP];
-    float4 x[C::XP];
+    uint4 x[C::XP];
 
-    __device__ __forceinline__ void load(const GemvJobs& jobs, const UnitPos& p, int batch,
-                                         int tid) {
-        const GemvJob& jb = jobs.j[p.job];
-        const int64_t cb0 = (int64_t)p.chunk * C::CRB;
+    __device__ __forceinline__ void load_w(const GemvJob& jb, const UnitPos& p, int tid) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(jb.w, (uint32_t)(jb.n * jb.rb));
+        const uint32_t cb0 = (uint32_t)p.chunk * C::CRB;
+        const uint32_t rb = (uint32_t)jb.rb;
+        const uint32_t base = (uint32_t)p.r0 * rb + cb0;
 #pragma unroll
         for (int i = 0; i < C::WP; ++i) {
             const int q = tid + 256 * i;
-            const int pr = q / C::PPR;
-            const int off = (q % C::PPR) * 16;
-            w[i] = make_uint4(0, 0, 0, 0);
-            if (q < C::WPIECES && p.r0 + pr < jb.n && cb0 + off < jb.rb)
-                w[i] = load_once16(jb.w + (p.r0 + pr) * jb.rb + cb0 + off);
+            const uint32_t pr = (uint32_t)q / C::PPR;
+            const uint32_t off = ((uint32_t)q % C::PPR) * 16;
+            const bool ok = q < C::WPIECES && cb0 + off < rb;
+            w[i] = buf_load16<true>(r, ok ? base + pr * rb + off : kOob);
         }
+    }
+
+    __device__ __forceinline__ void load_x(const GemvJob& jb, const UnitPos& p, int batch,
+                                           int tid) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(jb.x, (uint32_t)(batch * jb.ldx * 4));
         const int k0 = p.chunk * C::KC;
 #pragma unroll
         for (int i = 0; i < C::XP; ++i) {
             const int q = tid + 256 * i;
             const int b = q / (C::KC / 4);
             const int pos = (q % (C::KC / 4)) * 4;
-            x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (q < C::XPIECES && b < batch && k0 + pos < jb.k)
-                x[i] = *reinterpret_cast<const float4*>(jb.x + b * jb.ldx + k0 + pos);
+            const bool ok = q < C::XPIECES && k0 + pos < jb.k;
+            x[i] = buf_load16<false>(r, ok ? (uint32_t)((b * jb.ldx + k0 + pos) * 4) : kOob);
         }
     }
 
-    __device__ __forceinline__ void store(uint8_t* buf, int tid) const {
-        uint8_t* lw = buf;
-        float* lx = reinterpret_cast<float*>(buf + C::kWBytes);
-        float* lsum = reinterpret_cast<float*>(buf + C::kWBytes + C::kXBytes);
+    __device__ __forceinline__ void store_w(uint8_t* lw, int tid) const {
 #pragma unroll
         for (int i = 0; i < C::WP; ++i) {
             const int q = tid + 256 * i;
@@ -137,13 +155,18 @@ struct Prefetch {
                 *reinterpret_cast<uint4*>(lw + pr * C::WRS + off) = w[i];
             }
         }
+    }
+
+    __device__ __forceinline__ void store_x(uint8_t* xbuf, int tid) const {
+        float* lx = reinterpret_cast<float*>(xbuf);
+        float* lsum = reinterpret_cast<float*>(xbuf + C::kXBytes);
 #pragma unroll
         for (int i = 0; i < C::XP; ++i) {
             const int q = tid + 256 * i;
             if (C::XPIECES % 256 == 0 || q < C::XPIECES) {  // whole waves only
                 const int b = q / (C::KC / 4);
                 const int pos = (q % (C::KC / 4)) * 4;
-                const float4 v = x[i];
+                const float4 v = __builtin_bit_cast(float4, x[i]);
                 *reinterpret_cast<float4*>(lx + b * C::XBS + (pos >> 6) * C::XSS + (pos & 63)) = v;
                 if constexpr (FMT == kQ4_K) {
                     float t = (v.x + v.y) + (v.z + v.w);
@@ -158,94 +181,108 @@ struct Prefetch {
 };
 
 template <int FMT, int NB, int ROWS>
-__global__ __launch_bounds__(256) void gemv_stream_kernel(const GemvJobs jobs, int batch) {
+__device__ __forceinline__ void stream_compute(const GemvJobs& jobs, const UnitPos& cur,
+                                               const uint8_t* lw, const uint8_t* xbuf, int batch,
+                                               int s, int rl, float (&acc)[NB]) {
     using C = StreamCfg<FMT, NB, ROWS>;
     constexpr int SL = C::SL;
+    const GemvJob& jb = jobs.j[cur.job];
+    const float* lx = reinterpret_cast<const float*>(xbuf);
+    const float* lsum = reinterpret_cast<const float*>(xbuf + C::kXBytes);
+    const int k0 = cur.chunk * C::KC;
+    if (cur.r0 + rl < jb.n && k0 + s * 64 < jb.k) {
+        float f0[32], f1[32];
+        float sa0, sa1, mb0, mb1;
+        decode_unit<FMT>(lw + rl * C::WRS, s, f0, f1, sa0, sa1, mb0, mb1);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b < batch) {
+                const float4* xv = reinterpret_cast<const float4*>(lx + b * C::XBS + s * C::XSS);
+                float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float4 a = xv[i];
+                    float4 e = xv[8 + i];
+                    p0[i & 3] += f0[4 * i] * a.x + f0[4 * i + 1] * a.y + f0[4 * i + 2] * a.z +
+                                 f0[4 * i + 3] * a.w;
+                    p1[i & 3] += f1[4 * i] * e.x + f1[4 * i + 1] * e.y + f1[4 * i + 2] * e.z +
+                                 f1[4 * i + 3] * e.w;
+                }
+                float t = sa0 * ((p0[0] + p0[1]) + (p0[2] + p0[3])) +
+                          sa1 * ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+                if constexpr (FMT == kQ4_K) {
+                    const float* xs = lsum + (b * SL + s) * 2;
+                    t -= mb0 * xs[0] + mb1 * xs[1];
+                }
+                acc[b] += t;
+            }
+        }
+    }
+    if (cur.chunk == jb.nchunk - 1) {
+        // row finished: butterfly over the SL slice lanes of this row
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int o = 1; o < SL; o <<= 1) acc[b] += __shfl_xor(acc[b], o, 64);
+        }
+        if (s == 0 && cur.r0 + rl < jb.n) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (b < batch) jb.y[b * jb.ldy + cur.r0 + rl] = acc[b];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+    }
+}
+
+// One unit in flight in registers while the current one is computed from LDS.
+// Weights are double-buffered in LDS; the activation chunk is staged only when
+// the (matrix, chunk) changes -- for K <= KC that is once per matrix.
+template <int FMT, int NB, int ROWS>
+__global__ __launch_bounds__(256) void gemv_stream_kernel(const GemvJobs jobs, int batch) {
+    using C = StreamCfg<FMT, NB, ROWS>;
     extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t* lw0 = lds;
+    uint8_t* lx0 = lds + 2 * C::kWBytes;
     const int tid = threadIdx.x;
-    const int s = tid % SL;
-    const int rl = tid / SL;
+    const int s = tid % C::SL;
+    const int rl = tid / C::SL;
 
     if ((int)blockIdx.x >= jobs.total_tiles) return;
     Prefetch<FMT, NB, ROWS> pf;
     UnitPos cur = locate(jobs, blockIdx.x, 0, ROWS);
-    pf.load(jobs, cur, batch, tid);
-    pf.store(lds, tid);
+    pf.load_w(jobs.j[cur.job], cur, tid);
+    pf.load_x(jobs.j[cur.job], cur, batch, tid);
+    pf.store_w(lw0, tid);
+    pf.store_x(lx0, tid);
+    int xjob = cur.job, xchunk = cur.chunk, xb = 0;
     __syncthreads();
 
     float acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.f;
 
-    int buf = 0;
+    int wb = 0;
     for (;;) {
         UnitPos nxt;
-        bool more;
-        if (cur.chunk + 1 < jobs.j[cur.job].nchunk) {
-            more = true;
-            nxt = cur;
-            nxt.chunk = cur.chunk + 1;
-        } else {
-            const int tn = cur.tile + (int)gridDim.x;
-            more = tn < jobs.total_tiles;
-            if (more) nxt = locate(jobs, tn, 0, ROWS);
+        const bool more = next_unit<ROWS>(jobs, cur, nxt);
+        bool newx = false;
+        if (more) {
+            pf.load_w(jobs.j[nxt.job], nxt, tid);
+            newx = nxt.job != xjob || nxt.chunk != xchunk;
+            if (newx) pf.load_x(jobs.j[nxt.job], nxt, batch, tid);
         }
-        if (more) pf.load(jobs, nxt, batch, tid);
-        // ---- compute unit u from LDS buffer `buf` ----
-        {
-            const GemvJob& jb = jobs.j[cur.job];
-            const uint8_t* base = lds + buf * C::kBuf;
-            const uint8_t* lw = base;
-            const float* lx = reinterpret_cast<const float*>(base + C::kWBytes);
-            const float* lsum = reinterpret_cast<const float*>(base + C::kWBytes + C::kXBytes);
-            const int k0 = cur.chunk * C::KC;
-            if (cur.r0 + rl < jb.n && k0 + s * 64 < jb.k) {
-                float f0[32], f1[32];
-                float sa0, sa1, mb0, mb1;
-                decode_unit<FMT>(lw + rl * C::WRS, s, f0, f1, sa0, sa1, mb0, mb1);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (b < batch) {
-                        const float4* xv = reinterpret_cast<const float4*>(lx + b * C::XBS + s * C::XSS);
-                        float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            float4 a = xv[i];
-                            float4 e = xv[8 + i];
-                            p0[i & 3] += f0[4 * i] * a.x + f0[4 * i + 1] * a.y +
-                                         f0[4 * i + 2] * a.z + f0[4 * i + 3] * a.w;
-                            p1[i & 3] += f1[4 * i] * e.x + f1[4 * i + 1] * e.y +
-                                         f1[4 * i + 2] * e.z + f1[4 * i + 3] * e.w;
-                        }
-                        float t = sa0 * ((p0[0] + p0[1]) + (p0[2] + p0[3])) +
-                                  sa1 * ((p1[0] + p1[1]) + (p1[2] + p1[3]));
-                        if constexpr (FMT == kQ4_K) {
-                            const float* xs = lsum + (b * SL + s) * 2;
-                            t -= mb0 * xs[0] + mb1 * xs[1];
-                        }
-                        acc[b] += t;
-                    }
-                }
-            }
-            if (cur.chunk == jb.nchunk - 1) {
-                // row finished: butterfly over the SL slice lanes of this row
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-#pragma unroll
-                    for (int o = 1; o < SL; o <<= 1) acc[b] += __shfl_xor(acc[b], o, 64);
-                }
-                if (s == 0 && cur.r0 + rl < jb.n) {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        if (b < batch) jb.y[b * jb.ldy + cur.r0 + rl] = acc[b];
-                }
-#pragma unroll
-                for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-            }
-        }
+        stream_compute<FMT, NB, ROWS>(jobs, cur, lw0 + wb * C::kWBytes, lx0 + xb * C::kXBuf, batch,
+                                      s, rl, acc);
         if (!more) break;
-        buf ^= 1;
-        pf.store(lds + buf * C::kBuf, tid);
+        wb ^= 1;
+        pf.store_w(lw0 + wb * C::kWBytes, tid);
+        if (newx) {
+            xb ^= 1;
+            pf.store_x(lx0 + xb * C::kXBuf, tid);
+            xjob = nxt.job;
+            xchunk = nxt.chunk;
+        }
         __syncthreads();
         cur = nxt;
     }

@@ -90,6 +90,23 @@ __device__ __forceinline__ uint4 load_once16(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes
+// return zero, which is how tile and chunk edges are handled without branches.
+// Word 3 is the CDNA raw-buffer setting (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+constexpr uint32_t kOob = 0xFFFFFFF0u;  // an offset past any descriptor's range
+
+// 16-byte buffer load; `nt` marks data read exactly once (non-temporal).
+template <bool NT>
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -18,6 +18,9 @@ hipError_t launch_dequant(int type, const uint8_t* w, int64_t n, int64_t k, floa
                           hipStream_t s);
 
 int gemv_max_group();
+size_t gemv_mfma_ws_bytes(int type, int64_t k, int batch);
+hipError_t launch_gemv_mfma(int type, const GemvDesc* descs, int count, int batch, void* ws,
+                            hipStream_t s);
 hipError_t launch_gemv_group(int type, const GemvDesc* descs, int count, int batch, hipStream_t s);
 hipError_t launch_gemv(int type, const uint8_t* w, int64_t n, int64_t k, const float* x,
                        int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s);

@@ -57,21 +57,54 @@ D16 = 0x40000
 
 def test_gemv_validation(g):
     L = g._lib
-    assert L.quant_gemv(99, A16, 4, 32, B16, 32, C16, 4, 1, None) == UNSUP
-    assert L.quant_gemv(8, A16, 4, 33, B16, 33, C16, 4, 1, None) == ARG      # K % 32
-    assert L.quant_gemv(12, A16, 4, 512 + 32, B16, 544, C16, 4, 1, None) == ARG  # K % 256
-    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 4, 0, None) == ARG       # batch 0
-    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 4, 17, None) == ARG      # batch 17
-    assert L.quant_gemv(8, A16, 4, 64, B16, 32, C16, 4, 1, None) == ARG       # ldx < K
-    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 3, 1, None) == ARG       # ldy < N
-    assert L.quant_gemv(8, None, 4, 32, B16, 32, C16, 4, 1, None) == ARG
-    assert L.quant_gemv(8, A16, 4, 32, None, 32, C16, 4, 1, None) == ARG
-    assert L.quant_gemv(8, A16 + 2, 4, 32, B16, 32, C16, 4, 1, None) == ALIGN
-    assert L.quant_gemv(8, A16, 4, 32, B16 + 4, 32, C16, 4, 1, None) == ALIGN
-    assert L.quant_gemv(8, A16, 4, 32, B16, 34, C16, 4, 1, None) == ALIGN     # ldx % 4
-    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16 + 2, 4, 1, None) == ALIGN
-    assert L.quant_gemv(8, None, 0, 32, None, 32, None, 0, 1, None) == OK     # N == 0 no-op
-    assert L.quant_gemv(8, A16, -1, 32, B16, 32, C16, 4, 1, None) == ARG
+    assert L.quant_gemv(99, A16, 4, 32, B16, 32, C16, 4, 1, None, 0, None) == UNSUP
+    assert L.quant_gemv(8, A16, 4, 33, B16, 33, C16, 4, 1, None, 0, None) == ARG      # K % 32
+    assert L.quant_gemv(12, A16, 4, 512 + 32, B16, 544, C16, 4, 1, None, 0, None) == ARG  # K % 256
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 4, 0, None, 0, None) == ARG       # batch 0
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 4, 17, None, 0, None) == ARG      # batch 17
+    assert L.quant_gemv(8, A16, 4, 64, B16, 32, C16, 4, 1, None, 0, None) == ARG       # ldx < K
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16, 3, 1, None, 0, None) == ARG       # ldy < N
+    assert L.quant_gemv(8, None, 4, 32, B16, 32, C16, 4, 1, None, 0, None) == ARG
+    assert L.quant_gemv(8, A16, 4, 32, None, 32, C16, 4, 1, None, 0, None) == ARG
+    assert L.quant_gemv(8, A16 + 2, 4, 32, B16, 32, C16, 4, 1, None, 0, None) == ALIGN
+    assert L.quant_gemv(8, A16, 4, 32, B16 + 4, 32, C16, 4, 1, None, 0, None) == ALIGN
+    assert L.quant_gemv(8, A16, 4, 32, B16, 34, C16, 4, 1, None, 0, None) == ALIGN     # ldx % 4
+    assert L.quant_gemv(8, A16, 4, 32, B16, 32, C16 + 2, 4, 1, None, 0, None) == ALIGN
+    assert L.quant_gemv(8, None, 0, 32, None, 32, None, 0, 1, None, 0, None) == OK     # N == 0 no-op
+    assert L.quant_gemv(8, A16, -1, 32, B16, 32, C16, 4, 1, None, 0, None) == ARG
+
+
+def test_gemv_workspace_validation(g):
+    L = g._lib
+    need = L.quant_gemv_workspace_size(8, 2048, 8)
+    assert need >= 2048 // 32 * 1024
+    assert L.quant_gemv_workspace_size(8, 2048, 17) == 0
+    assert L.quant_gemv_workspace_size(12, 2000, 4) == 0
+    assert L.quant_gemv_workspace_size(12, 2560, 16) > L.quant_gemv_workspace_size(12, 2560, 8)
+    assert L.quant_gemv(8, A16, 4, 2048, B16, 2048, C16, 4, 8, D16, need - 1, None) == WS
+    assert L.quant_gemv(8, A16, 4, 2048, B16, 2048, C16, 4, 8, D16 + 16, need, None) == ALIGN
+
+
+def test_gemv_grouped_validation(g):
+    L = g._lib
+    arr = (g.GemvDesc * 3)()
+    for i in range(3):
+        arr[i] = g.GemvDesc(A16, 4, 2048, B16, 2048, C16, 4)
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert L.quant_gemv_grouped(8, p, 0, 1, None, 0, None) == ARG
+    assert L.quant_gemv_grouped(8, p, 17, 1, None, 0, None) == ARG
+    assert L.quant_gemv_grouped(8, None, 2, 1, None, 0, None) == ARG
+    assert L.quant_gemv_grouped(5, p, 2, 1, None, 0, None) == UNSUP
+    arr[1] = g.GemvDesc(A16, 4, 2047, B16, 2048, C16, 4)       # bad K in one member
+    assert L.quant_gemv_grouped(8, p, 3, 1, None, 0, None) == ARG
+    arr[1] = g.GemvDesc(A16 + 4, 4, 2048, B16, 2048, C16, 4)   # misaligned member
+    assert L.quant_gemv_grouped(8, p, 3, 1, None, 0, None) == ALIGN
+    arr[1] = g.GemvDesc(A16, 4, 2048, B16, 2048, C16, 4)
+    need = 3 * L.quant_gemv_workspace_size(8, 2048, 4)
+    assert L.quant_gemv_grouped(8, p, 3, 4, D16, need - 1, None) == WS
+    for i in range(3):
+        arr[i] = g.GemvDesc(None, 0, 2048, None, 2048, None, 0)  # all empty: no-op
+    assert L.quant_gemv_grouped(8, p, 3, 4, None, 0, None) == OK
 
 
 def test_dequant_validation(g):

@@ -68,10 +68,13 @@ def test_dequant_random_bit_exact(g, fmt, n, k):
 
 # --------------------------------------------------------------------------- #
 # GEMV
-def _gemv_case(g, fmt, n, k, b, seed=0, tid=1):
+PATHS = {"valu": None, "mfma": "auto"}   # no workspace -> vector units; workspace -> matrix cores
+
+
+def _gemv_case(g, fmt, n, k, b, seed=0, tid=1, ws=None):
     w = synth.quant_matrix(fmt, n, k, seed=seed, tensor_id=tid)
     x = synth.normal_f32((b, k), seed=seed, tensor_id=tid + 1)
-    y = host(g.quant_gemv(fmt, dev(w), n, k, dev(x)))
+    y = host(g.quant_gemv(fmt, dev(w), n, k, dev(x), ws=ws))
     yr, s = oracle.gemv(fmt, w, n, k, x)
     return y, yr, s, w, x
 
@@ -81,24 +84,26 @@ def _gemv_case(g, fmt, n, k, b, seed=0, tid=1):
     (Q8, 37, 2304, 1), (Q8, 37, 2304, 3), (Q8, 64, 6144, 8), (Q8, 65, 512, 16),
     (Q8, 5, 224, 1), (Q8, 9, 96, 6),            # K % 256 != 0 path
     (Q4, 70, 2560, 1), (Q4, 70, 2560, 4), (Q4, 33, 9728, 16), (Q4, 1, 256, 2),
-    (Q4, 300, 768, 5), (Q4, 17, 11264, 13),
+    (Q4, 300, 768, 5), (Q4, 17, 11264, 13), (Q8, 4099, 2048, 9), (Q4, 1000, 2560, 2),
 ])
-def test_gemv_parity(g, fmt, n, k, b):
-    say(f"gemv fmt={fmt} n={n} k={k} b={b}")
-    y, yr, s, _, _ = _gemv_case(g, fmt, n, k, b, tid=n * 7 + b)
+@pytest.mark.parametrize("path", PATHS)
+def test_gemv_parity(g, fmt, n, k, b, path):
+    say(f"gemv fmt={fmt} n={n} k={k} b={b} path={path}")
+    y, yr, s, _, _ = _gemv_case(g, fmt, n, k, b, tid=n * 7 + b, ws=PATHS[path])
     worst = check_rel(y, yr, s, GEMV_TOL, f"gemv {fmt} {n}x{k} b{b}")
     say(f"  worst err / bound = {worst:.3g}")
 
 
 @pytest.mark.parametrize("name,n,k", synth.DENSE_1B_LAYER_SET)
 @pytest.mark.parametrize("b", [1, 8])
-def test_gemv_dense_layer_set_full_size(g, name, n, k, b):
+@pytest.mark.parametrize("path", PATHS)
+def test_gemv_dense_layer_set_full_size(g, name, n, k, b, path):
     """The ~1B dense decode layer set (Q8_0) at batch 1 and 8, every row."""
-    say(f"gemv layer {name} {n}x{k} b={b}")
+    say(f"gemv layer {name} {n}x{k} b={b} path={path}")
     tid = synth.tid(1, n, k)
     w = synth.q8_0_matrix(n, k, seed=0, tensor_id=tid)
     x = synth.normal_f32((b, k), seed=0, tensor_id=tid + 1)
-    y = host(g.quant_gemv(Q8, dev(w), n, k, dev(x)))
+    y = host(g.quant_gemv(Q8, dev(w), n, k, dev(x), ws=PATHS[path]))
     yr, s = oracle.gemv(Q8, w, n, k, x)
     worst = check_rel(y, yr, s, GEMV_TOL, f"{name} b{b}")
     say(f"  worst err / bound = {worst:.3g}")
@@ -106,51 +111,58 @@ def test_gemv_dense_layer_set_full_size(g, name, n, k, b):
 
 @pytest.mark.parametrize("name,n,k", synth.Q4K_FFN_PAIR)
 @pytest.mark.parametrize("b", [1, 4, 16])
-def test_gemv_q4k_ffn_full_size(g, name, n, k, b):
-    say(f"gemv q4k {name} {n}x{k} b={b}")
+@pytest.mark.parametrize("path", PATHS)
+def test_gemv_q4k_ffn_full_size(g, name, n, k, b, path):
+    say(f"gemv q4k {name} {n}x{k} b={b} path={path}")
     tid = synth.tid(2, n, k)
     w = synth.q4_k_matrix(n, k, seed=0, tensor_id=tid)
     x = synth.normal_f32((b, k), seed=0, tensor_id=tid + 1)
-    y = host(g.quant_gemv(Q4, dev(w), n, k, dev(x)))
+    y = host(g.quant_gemv(Q4, dev(w), n, k, dev(x), ws=PATHS[path]))
     yr, s = oracle.gemv(Q4, w, n, k, x)
     worst = check_rel(y, yr, s, GEMV_TOL, f"{name} b{b}")
     say(f"  worst err / bound = {worst:.3g}")
 
 
-def test_gemv_one_hot_columns_exact(g):
-    """x = e_c gives the dequantized column c exactly (adds of zero are exact)."""
-    say("gemv one-hot")
+@pytest.mark.parametrize("path", PATHS)
+def test_gemv_one_hot_columns_exact(g, path):
+    """x = e_c gives the dequantized column c exactly (adds of zero are exact; on
+    the matrix cores the power-of-two scaling and the fp16 split are exact too)."""
+    say(f"gemv one-hot {path}")
     for fmt, n, k in ((Q8, 96, 2048), (Q4, 96, 2560)):
         w = synth.quant_matrix(fmt, n, k, seed=3, tensor_id=71)
         cols = [0, 31, 32, 255, 256, 1023, k - 1]
         x = np.zeros((len(cols), k), dtype=np.float32)
         for i, c in enumerate(cols):
             x[i, c] = 1.0
-        y = host(g.quant_gemv(fmt, dev(w), n, k, dev(x)))
+        y = host(g.quant_gemv(fmt, dev(w), n, k, dev(x), ws=PATHS[path]))
         dense = oracle.dequant(fmt, w, n, k)
         for i, c in enumerate(cols):
             assert np.array_equal(y[i], dense[:, c])
 
 
-def test_gemv_batch_equals_single_rows_and_is_deterministic(g):
-    say("gemv batch_check")
+@pytest.mark.parametrize("path", PATHS)
+def test_gemv_batch_equals_single_rows_and_is_deterministic(g, path):
+    say(f"gemv batch_check {path}")
+    ws = PATHS[path]
     for fmt, n, k in ((Q8, 200, 2048), (Q4, 200, 2560)):
         w = synth.quant_matrix(fmt, n, k, seed=4, tensor_id=72)
         x = synth.normal_f32((16, k), seed=4, tensor_id=73)
         wd, xd = dev(w), dev(x)
-        yb = host(g.quant_gemv(fmt, wd, n, k, xd))
-        yb2 = host(g.quant_gemv(fmt, wd, n, k, xd))
+        yb = host(g.quant_gemv(fmt, wd, n, k, xd, ws=ws))
+        yb2 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=ws))
         assert np.array_equal(yb, yb2)
         yr, s = oracle.gemv(fmt, w, n, k, x)
         for b in range(16):
-            y1 = host(g.quant_gemv(fmt, wd, n, k, dev(x[b:b + 1])))
+            y1 = host(g.quant_gemv(fmt, wd, n, k, dev(x[b:b + 1]), ws=ws))
             check_rel(y1, yr[b:b + 1], s[b:b + 1], GEMV_TOL, f"single row {b}")
             check_rel(yb[b:b + 1], yr[b:b + 1], s[b:b + 1], GEMV_TOL, f"batched row {b}")
 
 
-def test_gemv_integer_case_exact(g):
-    """d = 1 and small integer activations: every partial sum is an exact integer."""
-    say("gemv integer exact")
+@pytest.mark.parametrize("path", PATHS)
+def test_gemv_integer_case_exact(g, path):
+    """d = 1 and small integer activations: every partial sum is an exact integer
+    (on the matrix cores an exact multiple of the power-of-two scale)."""
+    say(f"gemv integer exact {path}")
     n, k = 130, 4096
     rng = np.random.default_rng(11)
     q = rng.integers(-127, 128, size=(n, k))
@@ -158,7 +170,7 @@ def test_gemv_integer_case_exact(g):
     raw[:, 0:2] = [0x00, 0x3C]
     raw[:, 2:] = q.reshape(-1, 32).astype(np.int8).view(np.uint8)
     x = rng.integers(-8, 9, size=(4, k)).astype(np.float32)
-    y = host(g.quant_gemv(Q8, dev(raw.reshape(n, -1)), n, k, dev(x)))
+    y = host(g.quant_gemv(Q8, dev(raw.reshape(n, -1)), n, k, dev(x), ws=PATHS[path]))
     ref = (x.astype(np.int64) @ q.T).astype(np.float32)
     assert np.array_equal(y, ref)
 
@@ -184,19 +196,20 @@ def _group_case(fmt, specs, b, seed=6):
     return mats
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("fmt,specs,b", [
     (Q8, [(3072, 2048), (2048, 2048), (6144, 2048), (6144, 2048), (2048, 6144), (4099, 2048)], 1),
     (Q8, [(300, 2048), (77, 6144), (5, 224), (129, 512)], 8),     # includes a K % 256 != 0 member
     (Q4, [(9728, 2560), (2560, 9728), (33, 256)], 4),
     (Q4, [(100, 2560), (1, 9728)], 16),
 ])
-def test_gemv_grouped_parity(g, fmt, specs, b):
-    say(f"gemv grouped fmt={fmt} b={b} {specs}")
+def test_gemv_grouped_parity(g, fmt, specs, b, path):
+    say(f"gemv grouped fmt={fmt} b={b} {specs} path={path}")
     mats = _group_case(fmt, specs, b)
     items = [(dev(w), n, k, dev(x), torch.empty((b, n), device="cuda")) for w, n, k, x in mats]
-    g.quant_gemv_grouped(fmt, items)
+    g.quant_gemv_grouped(fmt, items, ws=PATHS[path])
     first = [host(it[4]) for it in items]
-    g.GemvGroup(fmt, items)()
+    g.GemvGroup(fmt, items, ws=PATHS[path])()
     for (w, n, k, x), it, y0 in zip(mats, items, first):
         y = host(it[4])
         assert np.array_equal(y, y0)          # deterministic
@@ -210,7 +223,8 @@ def test_graph_replays_match_eager(g):
     say("graph replay")
     mats = _group_case(Q8, [(2048, 2048), (512, 6144)], 8)
     items = [(dev(w), n, k, dev(x), torch.empty((8, n), device="cuda")) for w, n, k, x in mats]
-    grp = g.GemvGroup(Q8, items)
+    grp = g.GemvGroup(Q8, items, ws="auto")
+    grp1 = g.GemvGroup(Q8, [(it[0], it[1], it[2], it[3][:1], it[4][:1].clone()) for it in items])
     wq = dev(synth.q4_k_matrix(256, 1024, seed=1, tensor_id=5))
     a = dev(synth.normal_f32((64, 1024), seed=1, tensor_id=6))
     c = torch.empty((64, 256), device="cuda")
@@ -225,12 +239,14 @@ def test_graph_replays_match_eager(g):
 
     def work():
         grp()
+        grp1()
         g.quant_gemm(Q4, wq, 256, 1024, a, c, ws)
         ii, pp, _ = g.moe_route(wr, x, k)
         idx.copy_(ii)
         g.moe_expert_gemv(Q4, wg, wu, wd, e, h, f, x, ii, pp, ym, mws)
 
-    outs = lambda: [host(it[4]).copy() for it in items] + [host(c).copy(), host(ym).copy(), host(idx).copy()]
+    outs = lambda: ([host(it[4]).copy() for it in items] + [host(it[4]).copy() for it in grp1._keep]
+                    + [host(c).copy(), host(ym).copy(), host(idx).copy()])
     work()
     ref = outs()
     side = torch.cuda.Stream()
