@@ -204,7 +204,9 @@ struct MCfg {
     static constexpr int RWG = 16 * WM;                         // rows per workgroup
     static constexpr int KC = FMT == kQ8_0 ? 256 : 512;         // weights per chunk
     static constexpr int CRB = FMT == kQ8_0 ? 272 : 288;        // bytes per row chunk
-    static constexpr int RS = CRB + 16;                         // LDS row stride
+    // LDS row stride: 68 dwords (Q8_0) / 76 dwords (Q4_K) put the 16 rows a wave
+    // reads at distinct multiples of 4 banks, so 64 lanes x 2 dwords spread evenly.
+    static constexpr int RS = FMT == kQ8_0 ? CRB : CRB + 16;
     static constexpr int NBLK = KC / 32;                        // 32-wide steps per chunk
     static constexpr int NSB = FMT == kQ4_K ? KC / 256 : 0;
     static constexpr int kW = RWG * RS;
@@ -334,28 +336,36 @@ __device__ __forceinline__ void mfma_unit(const MJobs& jobs, const MPos& cur, ui
             const int k0 = cur.chunk * C::KC;
             if constexpr (FMT == kQ8_0) {
                 // K is a multiple of the chunk here, so every block is present.
-                constexpr int NPW = C::NBLK / WK;
+                // Blocks are taken in pairs (68 bytes, dword aligned): the even
+                // block's quants start 2 bytes into a dword and are realigned, the
+                // odd block's are aligned; its scale is the high half of dword 8.
+                constexpr int NPW = C::NBLK / WK;   // blocks per wave: pairs wk, wk+WK, ...
+                static_assert(NPW % 2 == 0, "blocks per wave come in pairs");
                 f16x8 bop[NPW];
                 float dq[NPW];
+                const uint32_t* rowd = reinterpret_cast<const uint32_t*>(wrow);
 #pragma unroll
-                for (int i = 0; i < NPW; ++i) {
-                    const int bi = wk + WK * i;
-                    const uint16_t* hw = reinterpret_cast<const uint16_t*>(wrow + bi * kQ8Bytes);
-                    dq[i] = half_bits_to_float(hw[0]);
-                    // quants 8h .. 8h+7 start at byte 2 + 8h of the block
-                    const uint32_t v0 = (uint32_t)hw[1 + 4 * h] | ((uint32_t)hw[2 + 4 * h] << 16);
-                    const uint32_t v1 = (uint32_t)hw[3 + 4 * h] | ((uint32_t)hw[4 + 4 * h] << 16);
+                for (int i = 0; i < NPW; i += 2) {
+                    const int pr = wk + WK * (i >> 1);   // pair index in the chunk
+                    const uint32_t* pd = rowd + 17 * pr;
+                    const uint32_t e0 = pd[2 * h], e1 = pd[2 * h + 1], e2 = pd[2 * h + 2];
+                    const uint32_t o0 = pd[9 + 2 * h], o1 = pd[10 + 2 * h];
+                    dq[i] = half_bits_to_float(pd[0]);
+                    dq[i + 1] = half_bits_to_float(pd[8] >> 16);
                     uint32_t b4[4];
-                    q8x4_to_f16(v0, b4[0], b4[1]);
-                    q8x4_to_f16(v1, b4[2], b4[3]);
+                    q8x4_to_f16(__builtin_amdgcn_alignbyte(e1, e0, 2), b4[0], b4[1]);
+                    q8x4_to_f16(__builtin_amdgcn_alignbyte(e2, e1, 2), b4[2], b4[3]);
                     bop[i] = __builtin_bit_cast(f16x8, make_uint4(b4[0], b4[1], b4[2], b4[3]));
+                    q8x4_to_f16(o0, b4[0], b4[1]);
+                    q8x4_to_f16(o1, b4[2], b4[3]);
+                    bop[i + 1] = __builtin_bit_cast(f16x8, make_uint4(b4[0], b4[1], b4[2], b4[3]));
                 }
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     f32x4 dv[NPW];
 #pragma unroll
                     for (int i = 0; i < NPW; ++i) {
-                        const int bi = wk + WK * i;
+                        const int bi = 2 * (wk + WK * (i >> 1)) + (i & 1);
                         const f16x8 aop = *reinterpret_cast<const f16x8*>(
                             frag + (t * C::NBLK + bi) * 1024 + lane * 16);
                         dv[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[i],
