@@ -79,10 +79,15 @@ struct MJobs {
 // ------------------------------------------------------------------ prep ----
 // One workgroup per (job, padded batch row b).  Rows b >= batch write zeros so the
 // padded MFMA rows contribute nothing.
+// blockIdx.y splits K into slices of kXfragSlice blocks; every slice recomputes
+// the row's maximum (a cheap read of K floats) so the slices need no exchange.
+constexpr int kXfragSlice = 32;
+
 template <int FMT>
 __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch, int mt) {
     const int job = blockIdx.x / (mt * 8);
     const int b = blockIdx.x % (mt * 8);
+    const int slice = blockIdx.y;
     const MJob& jb = jobs.j[job];
     const int k = jb.k;
     const XfLayout L = xf_layout(FMT, k, mt);
@@ -115,14 +120,15 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
     }
     const int t = b / 8;          // M tile
     const int bb = b % 8;         // row pair within the tile
-    if (tid == 0) reinterpret_cast<float*>(jb.xf + L.inv)[b] = live ? inv : 1.f;
+    if (tid == 0 && slice == 0) reinterpret_cast<float*>(jb.xf + L.inv)[b] = live ? inv : 1.f;
 
     // A-operand fragments of v_mfma_f32_16x16x32_f16: lane l = i + 16*h holds
     // A[i][8h .. 8h+7]; rows i = 2*bb (hi) and 2*bb + 1 (lo).
     _Float16* frag = reinterpret_cast<_Float16*>(jb.xf + L.frag);
     const int nblk = k / 32;
-#pragma unroll 4
-    for (int q = tid; q < nblk * 4; q += 256) {
+    const int q_end = min(nblk, (slice + 1) * kXfragSlice) * 4;
+    if (slice * kXfragSlice >= nblk) return;
+    for (int q = slice * kXfragSlice * 4 + tid; q < q_end; q += 256) {
         const int blk = q >> 2;
         const int h = q & 3;
         float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -150,7 +156,9 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
         _Float16* mins = reinterpret_cast<_Float16*>(jb.xf + L.mins);
         const int nsb = k / 256;
         const float sc5 = sc * (1.f / 32.f);
-        for (int q = tid; q < nsb * 2; q += 256) {
+        // super-blocks whose sub-blocks start in this slice
+        const int sb0 = slice * kXfragSlice / 8, sb1 = min(nsb, (slice + 1) * kXfragSlice / 8);
+        for (int q = sb0 * 2 + tid; q < sb1 * 2; q += 256) {
             const int sb = q >> 1;
             const int hq = q & 1;
             f16x4 hi, lo;
@@ -597,11 +605,14 @@ hipError_t launch_gemv_mfma(int type, const GemvDesc* descs, int count, int batc
         p += gemv_mfma_ws_bytes(type, d.k, batch);
     }
     if (jobs.count == 0) return hipSuccess;
-    const unsigned pgrid = (unsigned)(jobs.count * mt * 8);
+    int64_t kmax = 0;
+    for (int i = 0; i < jobs.count; ++i) kmax = jobs.j[i].k > kmax ? jobs.j[i].k : kmax;
+    const dim3 pgrid((unsigned)(jobs.count * mt * 8),
+                     (unsigned)((kmax / 32 + kXfragSlice - 1) / kXfragSlice));
     if (type == kQ4_K)
-        hipLaunchKernelGGL(xfrag_kernel<kQ4_K>, dim3(pgrid), dim3(256), 0, s, jobs, batch, mt);
+        hipLaunchKernelGGL(xfrag_kernel<kQ4_K>, pgrid, dim3(256), 0, s, jobs, batch, mt);
     else
-        hipLaunchKernelGGL(xfrag_kernel<kQ8_0>, dim3(pgrid), dim3(256), 0, s, jobs, batch, mt);
+        hipLaunchKernelGGL(xfrag_kernel<kQ8_0>, pgrid, dim3(256), 0, s, jobs, batch, mt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (type == kQ4_K)
