@@ -140,7 +140,11 @@ int quant_gemm(int type, const void* w, int64_t n, int64_t k, const float* a, in
     const int blk = block_of(type);
     if (!blk || mode != GGQ_GEMM_BF16) return GGQ_ERR_UNSUPPORTED;
     if (n < 0 || m < 0 || k <= 0 || k % blk != 0 || lda < k || ldc < n) return GGQ_ERR_ARG;
-    if (n > (int64_t)INT_MAX * 16 || m > (int64_t)65535 * 128) return GGQ_ERR_ARG;
+    if (n > (int64_t)INT_MAX || m > (int64_t)INT_MAX) return GGQ_ERR_ARG;
+    // the bf16 copy of A is addressed with 32-bit buffer offsets
+    if ((m + 15) / 16 * 16 * ((k + 255) / 256 * 256) * 2 >= ((int64_t)1 << 31)) return GGQ_ERR_ARG;
+    // ... and so are the weight blocks
+    if (n * ggq::row_bytes(type, k) >= ((int64_t)1 << 32)) return GGQ_ERR_ARG;
     if (m == 0 || n == 0) return GGQ_OK;
     if (!w || !a || !c) return GGQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(a, 16) || lda % 4 != 0 || !aligned(c, 4)) return GGQ_ERR_ALIGN;

@@ -2,17 +2,38 @@
 // W in Q8_0 / Q4_K blocks (phobos-bench pp<N>, Phobos README "Command-Line
 // Tools"; the pages report prompt processing as their weaker path).
 //
-// This is the one dense contraction on the path, so it runs on the matrix cores:
-//  1. prep : A fp32 -> bf16 (round to nearest even) into the workspace, rows
-//            padded with zeros to a multiple of 64 columns.
-//  2. main : 256-thread workgroups own a BM x BN tile of C (BM = 128, four waves
-//            of 32 rows each, BN = 16*NT).  Per 64-wide K step the A tile is
-//            copied to LDS and the W tile is decoded from its blocks straight to
-//            bf16 in LDS (each weight decoded once per workgroup and reused by all
-//            BM rows), then every wave runs v_mfma_f32_16x16x32_bf16 over its
-//            32 x BN sub-tile with fp32 accumulators.
+// This is the one dense contraction on the path, so it runs on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+//  1. prep   : A fp32 -> bf16 (round to nearest even) into the workspace, K
+//              padded with zeros to a multiple of 256 and M to a multiple of
+//              16, stored in MFMA fragment order: for each 64-wide K step, each
+//              group of 16 rows and each 32-wide half, the 64 lanes' 8-element
+//              fragments lie in one contiguous KiB.  A fragment load is then one
+//              fully used, contiguous KiB (8 cache lines) instead of 16 half
+//              lines, which halves the work of the vector memory pipeline that
+//              bounds this kernel.
+//  2. main   : a workgroup of WV waves owns a (64*WV) x BN tile of C; wave w owns
+//              rows 64w .. 64w+63 and all BN = 16*NT columns (4 x NT MFMA
+//              sub-tiles, accumulators in registers).  Per 64-wide K step:
+//              * the W tile (BN rows x 64) is decoded from its blocks to bf16
+//                exactly once per workgroup, spread evenly over the waves, into
+//                one of two LDS buffers; every wave reads all of it;
+//              * each wave loads its own A fragments straight from the bf16 copy
+//                (no sharing between waves, so no LDS round trip), one step
+//                ahead of the MFMAs that use them;
+//              * the next step's raw W bytes are fetched while this step's MFMAs
+//                run, then decoded into the other buffer: one barrier per step.
+//              With 8 waves (two per SIMD) one wave's decode overlaps the other
+//              wave's MFMAs.  LDS rows are 144 bytes apart, so the 16 rows of a
+//              fragment read land on distinct bank groups.
+//              Column tiles may overlap (stride < BN) so the tile count fits the
+//              256 compute units; overlapped columns are computed twice, stored
+//              once.  Rows past M and N are clamped to the last valid row: they
+//              compute finite values that are never stored.
+//  3. reduce : long K may be split over S workgroups writing fp32 partials; they
+//              are summed in split order (deterministic, no atomics).
 // Rounding: A and the decoded weights are each rounded once to bf16 (relative
-// error <= 2^-9 each); products and sums are fp32.
+// error <= 2^-9 each); products are exact in fp32 and sums accumulate in fp32.
 #include "ggq_device.h"
 #include "ggq_launch.h"
 
@@ -21,191 +42,438 @@ namespace ggq {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int kBM = 128;
-constexpr int kBK = 64;
-constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row (16-byte pad)
+constexpr int kKAlign = 256;
+constexpr int kBK = 64;            // K per step
+constexpr int kLRow = kBK + 8;     // bf16 per LDS row: 144 bytes
+constexpr int kDW = 4;             // steps of raw W bytes in flight
 
-inline int64_t kpad(int64_t k) { return (k + kBK - 1) / kBK * kBK; }
+inline int64_t kpad(int64_t k) { return (k + kKAlign - 1) / kKAlign * kKAlign; }
+
+// Hardware round-to-nearest-even conversion of two floats to packed bf16.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+__host__ __device__ inline int64_t mpad(int64_t m) { return (m + 15) / 16 * 16; }
+
+// Byte offset of the fragment (16-row group g, K step st, half h, lane l) in the
+// fragment-ordered copy with `groups` row groups.
+__host__ __device__ inline int64_t frag_offset(int64_t st, int64_t g, int h, int l, int64_t groups) {
+    return (((st * groups + g) * 2 + h) * 64 + l) * 16;
+}
 
 __global__ __launch_bounds__(256) void prep_bf16_kernel(const float* __restrict__ a, int64_t lda,
                                                         int64_t m, int64_t k, int64_t kp,
                                                         uint16_t* __restrict__ out) {
     const int64_t q = kp / 4;
+    const int64_t m16 = mpad(m);
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= m * q) return;
+    if (i >= m16 * q) return;
     const int64_t row = i / q;
     const int64_t col = (i % q) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (col < k) v = *reinterpret_cast<const float4*>(a + row * lda + col);
+    if (row < m && col < k) v = *reinterpret_cast<const float4*>(a + row * lda + col);
     uint2 o;
-    o.x = pack_bf16x2(v.x, v.y);
-    o.y = pack_bf16x2(v.z, v.w);
-    *reinterpret_cast<uint2*>(out + row * kp + col) = o;
+    o.x = cvt_bf16x2(v.x, v.y);
+    o.y = cvt_bf16x2(v.z, v.w);
+    // element (row, col): step col/64, half (col%64)/32, lane row%16 + 16*((col%32)/8)
+    const int cc = (int)(col % kBK);
+    const int lane = (int)(row % 16) + 16 * ((cc % 32) / 8);
+    const int64_t off = frag_offset(col / kBK, row / 16, cc / 32, lane, m16 / 16) + 2 * (cc % 8);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(out) + off) = o;
 }
 
-// Decode 32 weights of W row `nrow` for K step k0 into bf16 LDS row `dst`.
-// Thread half h selects which 32: Q8_0 block (k0/32 + h); Q4_K quant bytes
-// 16h..16h+15 of the step's 64-weight group (16 low-nibble and 16 high-nibble
-// weights, at local columns 16h.. and 32+16h..).
+// One decode unit = 16 weights of one W row in the current step.
+//  Q4_K: the step is 64-weight group g = (k0/64)%4 of super-block k0/256; unit u
+//        (0..3) holds quant bytes 32g + 8u .. +7, i.e. step columns 8u + i (low
+//        nibbles, sub-block 2g) and 32 + 8u + i (high nibbles, sub-block 2g+1).
+//  Q8_0: unit h (0..3) is half h%2 of block k0/32 + h/2: step columns 16h .. +15.
 template <int FMT>
-__device__ __forceinline__ void decode_w32(const uint8_t* __restrict__ w, int64_t nrow, bool ok,
-                                           int64_t rb, int64_t k, int k0, int h, uint16_t* dst) {
-    uint32_t o[16];
-    if constexpr (FMT == kQ8_0) {
-        const int64_t kb = k0 / 32 + h;
-        if (ok && kb < k / 32) {
-            const uint16_t* p = reinterpret_cast<const uint16_t*>(w + nrow * rb + kb * kQ8Bytes);
-            float d = half_bits_to_float(p[0]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint32_t v = p[1 + i];
-                o[i] = pack_bf16x2(d * sbyte_f(v, 0), d * sbyte_f(v, 1));
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[i] = 0;
-        }
-        uint4* d4 = reinterpret_cast<uint4*>(dst + 32 * h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d4[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+struct RawUnit;
+template <>
+struct RawUnit<kQ4_K> {
+    u32x4 hdr;   // d | dmin, packed scales
+    uint32_t q0, q1;
+};
+template <>
+struct RawUnit<kQ8_0> {
+    uint32_t d;      // scale bits (low half)
+    u32x4 x;         // 16 bytes from the dword-aligned start of the quants
+    uint32_t x4;     // the two bytes after them
+    uint32_t sh;     // byte misalignment of the quants (0 or 2)
+};
+
+struct WView {
+    __amdgpu_buffer_rsrc_t rsrc;   // over the whole matrix
+    int64_t n, rb, nblk;           // rows, bytes per row, Q8_0 blocks per row
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_unit(const WView& v, int64_t row, int k0, int u,
+                                          RawUnit<FMT>& r) {
+    row = row < v.n ? row : v.n - 1;
+    const uint32_t rowoff = (uint32_t)(row * v.rb);
+    if constexpr (FMT == kQ4_K) {
+        const uint32_t sb = rowoff + (uint32_t)(k0 / 256) * kQ4Bytes;
+        r.hdr = __builtin_amdgcn_raw_buffer_load_b128(v.rsrc, sb, 0, 0);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(
+            v.rsrc, sb + 16 + 32 * ((k0 / 64) & 3) + 8 * u, 0, 0);
+        r.q0 = q.x;
+        r.q1 = q.y;
     } else {
-        if (ok) {
-            const uint8_t* sb = w + nrow * rb + (int64_t)(k0 / 256) * kQ4Bytes;
-            const int g = (k0 / 64) & 3;
-            uint4 hd = *reinterpret_cast<const uint4*>(sb);
-            uint4 qv = *reinterpret_cast<const uint4*>(sb + 16 + 32 * g + 16 * h);
-            float d = half_bits_to_float(hd.x);
-            float dmin = half_bits_to_float(hd.x >> 16);
-            Q4KScales sc = q4k_unpack(hd.y, hd.z, hd.w);
-            uint32_t sc0, m0, sc1, m1;
-            q4k_sub(sc, 2 * g, sc0, m0);
-            q4k_sub(sc, 2 * g + 1, sc1, m1);
-            const float a0 = d * (float)sc0, b0 = dmin * (float)m0;
-            const float a1 = d * (float)sc1, b1 = dmin * (float)m1;
-            const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t lo = qw[i] & 0x0F0F0F0Fu;
-                uint32_t hi = (qw[i] >> 4) & 0x0F0F0F0Fu;
-                o[2 * i] = pack_bf16x2(a0 * ubyte_f(lo, 0) - b0, a0 * ubyte_f(lo, 1) - b0);
-                o[2 * i + 1] = pack_bf16x2(a0 * ubyte_f(lo, 2) - b0, a0 * ubyte_f(lo, 3) - b0);
-                o[8 + 2 * i] = pack_bf16x2(a1 * ubyte_f(hi, 0) - b1, a1 * ubyte_f(hi, 1) - b1);
-                o[8 + 2 * i + 1] = pack_bf16x2(a1 * ubyte_f(hi, 2) - b1, a1 * ubyte_f(hi, 3) - b1);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[i] = 0;
-        }
-        uint4* lo4 = reinterpret_cast<uint4*>(dst + 16 * h);
-        uint4* hi4 = reinterpret_cast<uint4*>(dst + 32 + 16 * h);
-        lo4[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        lo4[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        hi4[0] = make_uint4(o[8], o[9], o[10], o[11]);
-        hi4[1] = make_uint4(o[12], o[13], o[14], o[15]);
+        int64_t blk = k0 / 32 + (u >> 1);
+        blk = blk < v.nblk ? blk : v.nblk - 1;   // K tail: finite weights times zero A
+        const uint32_t b = rowoff + (uint32_t)blk * kQ8Bytes;
+        const uint32_t o = b + 2 + 16 * (u & 1);
+        const uint32_t base = o & ~3u;
+        r.sh = o & 3u;
+        r.d = __builtin_amdgcn_raw_buffer_load_b16(v.rsrc, b, 0, 0);
+        r.x = __builtin_amdgcn_raw_buffer_load_b128(v.rsrc, base, 0, 0);
+        // only the first two bytes of the next dword are used (when sh == 2); a
+        // 2-byte load keeps the read inside the block
+        r.x4 = __builtin_amdgcn_raw_buffer_load_b16(v.rsrc, base + 16, 0, 0);
     }
 }
 
-template <int FMT, int NT>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w, int64_t n,
-                                                   int64_t k, int64_t rb,
-                                                   const uint16_t* __restrict__ abf, int64_t kp,
-                                                   int64_t m, float* __restrict__ c, int64_t ldc) {
-    constexpr int BN = 16 * NT;
-    __shared__ __align__(16) uint16_t As[kBM * kLdsRow];
-    __shared__ __align__(16) uint16_t Ws[BN * kLdsRow];
+// Decode one unit into 16 bf16 weights of LDS row `dst` (bf16 elements).
+template <int FMT>
+__device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int k0, uint16_t* dst) {
+    if constexpr (FMT == kQ4_K) {
+        const int g = (k0 / 64) & 3;
+        const float d = half_bits_to_float(r.hdr.x);
+        const float dmin = half_bits_to_float(r.hdr.x >> 16);
+        const Q4KScales sc = q4k_unpack(r.hdr.y, r.hdr.z, r.hdr.w);
+        uint32_t sc0, m0, sc1, m1;
+        q4k_sub(sc, 2 * g, sc0, m0);
+        q4k_sub(sc, 2 * g + 1, sc1, m1);
+        const float a0 = d * (float)sc0, b0 = -dmin * (float)m0;
+        const float a1 = d * (float)sc1, b1 = -dmin * (float)m1;
+        const uint32_t qw[2] = {r.q0, r.q1};
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t l = qw[i] & 0x0F0F0F0Fu;
+            const uint32_t h = (qw[i] >> 4) & 0x0F0F0F0Fu;
+            lo[2 * i] = cvt_bf16x2(__builtin_fmaf(a0, ubyte_f(l, 0), b0), __builtin_fmaf(a0, ubyte_f(l, 1), b0));
+            lo[2 * i + 1] = cvt_bf16x2(__builtin_fmaf(a0, ubyte_f(l, 2), b0), __builtin_fmaf(a0, ubyte_f(l, 3), b0));
+            hi[2 * i] = cvt_bf16x2(__builtin_fmaf(a1, ubyte_f(h, 0), b1), __builtin_fmaf(a1, ubyte_f(h, 1), b1));
+            hi[2 * i + 1] = cvt_bf16x2(__builtin_fmaf(a1, ubyte_f(h, 2), b1), __builtin_fmaf(a1, ubyte_f(h, 3), b1));
+        }
+        *reinterpret_cast<uint4*>(dst + 8 * u) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<uint4*>(dst + 32 + 8 * u) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    } else {
+        (void)k0;
+        // (q ^ 0x80) read as an unsigned byte is q + 128; d*(q+128) - 128d = d*q
+        // exactly (both products fit in fp32's mantissa).
+        const float d = half_bits_to_float(r.d);
+        const float nd = -128.f * d;
+        const uint32_t xs[5] = {r.x.x, r.x.y, r.x.z, r.x.w, r.x4};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t qd = __builtin_amdgcn_alignbyte(xs[i + 1], xs[i], r.sh) ^ 0x80808080u;
+            o[2 * i] = cvt_bf16x2(__builtin_fmaf(d, ubyte_f(qd, 0), nd), __builtin_fmaf(d, ubyte_f(qd, 1), nd));
+            o[2 * i + 1] = cvt_bf16x2(__builtin_fmaf(d, ubyte_f(qd, 2), nd), __builtin_fmaf(d, ubyte_f(qd, 3), nd));
+        }
+        uint4* d4 = reinterpret_cast<uint4*>(dst + 16 * u);
+        d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+template <int WV, int NT>
+struct GemmShape {
+    static constexpr int THREADS = 64 * WV;
+    static constexpr int BM = 64 * WV;
+    static constexpr int BN = 16 * NT;
+    static constexpr int UNITS = BN * (kBK / 16);            // decode units per step
+    static constexpr int UPW = (UNITS + WV - 1) / WV;       // per wave
+    static constexpr int UPT = (UPW + 63) / 64;             // per thread
+    static constexpr int kBuf = BN * kLRow;                 // bf16 elements per buffer
+    static constexpr int kLds = 2 * kBuf * 2;               // bytes
+};
+
+struct GemmArgs {
+    const uint8_t* w;
+    const uint16_t* abf;   // fragment-ordered bf16 copy of A (see frag_offset)
+    float* c;              // output (S == 1) or partials [S][M][N]
+    int64_t n, k, rb, kp, m, ldc;
+    int32_t stride;        // column-tile stride (<= BN)
+    int32_t tiles_m, tiles_n, splits;
+    int32_t ksteps_per_split;
+};
+
+template <int FMT, int WV, int NT>
+__global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
+    using S = GemmShape<WV, NT>;
+    extern __shared__ __align__(16) uint16_t wl[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * kBM;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    f32x4 acc[2][NT];
+    // tile index: split-K fastest, then M, then N
+    int t = blockIdx.x;
+    const int split = t % p.splits;
+    t /= p.splits;
+    const int tm = t % p.tiles_m;
+    const int tn = t / p.tiles_m;
+    const int64_t m0 = (int64_t)tm * S::BM + 64 * wave;
+    const int64_t n0 = (int64_t)tn * p.stride;
+    const int kstep0 = split * p.ksteps_per_split;
+    const int nk = min(p.ksteps_per_split, (int)(p.kp / kBK) - kstep0);
+
+    WView wv;
+    wv.rsrc = make_rsrc(p.w, (uint32_t)(p.n * p.rb));
+    wv.n = p.n;
+    wv.rb = p.rb;
+    wv.nblk = p.k / 32;
+
+    f32x4 acc[4][NT];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nsteps = (int)(kp / kBK);
-    for (int ks = 0; ks < nsteps; ++ks) {
-        const int k0 = ks * kBK;
-        // A tile: 128 rows x 64 bf16 = 1024 16-byte pieces
+    // A fragments: sub-tile i, lane l -> row m0 + 16i + l%16, columns 8(l/16) .. +7
+    // of each 32-wide half of the step.  Row groups past the padded M read the
+    // last group (finite values, never stored).
+    const int64_t groups = mpad(p.m) / 16;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.abf, (uint32_t)(groups * 16 * p.kp * 2));
+    uint32_t aoff[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int p = tid + 256 * i;
-            int row = p >> 3;
-            int col = (p & 7) * 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m0 + row < m) v = *reinterpret_cast<const uint4*>(abf + (m0 + row) * kp + k0 + col);
-            *reinterpret_cast<uint4*>(As + row * kLdsRow + col) = v;
-        }
-        // W tile: BN rows x 64 weights, two threads per row
-        for (int p = tid; p < 2 * BN; p += 256) {
-            int nn = p >> 1;
-            int h = p & 1;
-            decode_w32<FMT>(w, n0 + nn, n0 + nn < n, rb, k, k0, h, Ws + nn * kLdsRow);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            bf16x8 af[2];
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
-                const uint16_t* src = As + (32 * wv + 16 * mi + (lane & 15)) * kLdsRow + kk + 8 * (lane >> 4);
-                af[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src));
-            }
-#pragma unroll
-            for (int nj = 0; nj < NT; ++nj) {
-                const uint16_t* src = Ws + (16 * nj + (lane & 15)) * kLdsRow + kk + 8 * (lane >> 4);
-                bf16x8 bfr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src));
-#pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr, acc[mi][nj], 0, 0, 0);
-            }
-        }
-        __syncthreads();
+    for (int i = 0; i < 4; ++i) {
+        int64_t g = (m0 + 16 * i) / 16;
+        g = g < groups ? g : groups - 1;
+        aoff[i] = (uint32_t)frag_offset(0, g, 0, lane, groups);
     }
-    // D[i][j]: lane holds rows 4*(lane/16) + r, column lane%16
+    const uint32_t astep = (uint32_t)(groups * 2048);   // bytes per K step
+    bf16x8 af[2][4], an[2][4];
+    // decode units of this thread: wave w takes units UPW*w .. UPW*w + UPW-1,
+    // unit q = row q / 4, part q % 4: four consecutive lanes read one row's bytes
+    // of the step together, so a load instruction touches few cache lines
+    RawUnit<FMT> ru[kDW][S::UPT];
+
+    // The loop body is unrolled kDW times so that every register ring index is a
+    // compile-time constant; the step count is rounded up to a multiple of kDW
+    // and the extra steps multiply zeros (their A loads lie past the
+    // descriptor's range), so no step needs a branch or a variable wait count.
+    const int nsteps = (nk + kDW - 1) / kDW * kDW;
+    auto load_a = [&](int ks, bf16x8 (&dst)[2][4]) {
+        const bool valid = ks < nk;
+        const uint32_t kb = (uint32_t)(kstep0 + ks) * astep;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int nj = 0; nj < NT; ++nj) {
-            const int64_t col = n0 + 16 * nj + (lane & 15);
+            for (int i = 0; i < 4; ++i)
+                dst[h][i] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                ra, valid ? aoff[i] + kb + 1024 * h : kOob, 0, 0));
+    };
+    // Lanes past a wave's share load a valid unit too (and never store it).
+    auto unit_of = [&](int i) {
+        const int q = S::UPW * wave + min(lane + 64 * i, S::UPW - 1);
+        return min(q, S::UNITS - 1);
+    };
+    auto load_w = [&](int ks, RawUnit<FMT> (&dst)[S::UPT]) {
+        const int step = kstep0 + min(ks, nk - 1);
+#pragma unroll
+        for (int i = 0; i < S::UPT; ++i) {
+            const int q = unit_of(i);
+            load_unit<FMT>(wv, n0 + q / 4, step * kBK, q % 4, dst[i]);
+        }
+    };
+    auto store_w = [&](int ks, const RawUnit<FMT> (&src)[S::UPT], uint16_t* buf) {
+        const int step = kstep0 + min(ks, nk - 1);
+#pragma unroll
+        for (int i = 0; i < S::UPT; ++i) {
+            const int qi = lane + 64 * i;
+            const int q = S::UPW * wave + qi;
+            if (qi < S::UPW && q < S::UNITS)
+                store_unit<FMT>(src[i], q % 4, step * kBK, buf + (q / 4) * kLRow);
+        }
+    };
+
+    if (nk > 0) {
+#pragma unroll
+        for (int d = 0; d < kDW; ++d) load_w(d, ru[d]);
+        load_a(0, af);
+        store_w(0, ru[0], wl);
+    }
+    __syncthreads();
+    for (int ks0 = 0; ks0 < nsteps; ks0 += kDW) {
+#pragma unroll
+        for (int d = 0; d < kDW; ++d) {
+            const int ks = ks0 + d;
+            bf16x8 (&acur)[2][4] = (d & 1) ? an : af;
+            bf16x8 (&anext)[2][4] = (d & 1) ? af : an;
+            // ring slot d held step ks (decoded during the previous step): refill
+            // it with step ks + kDW, and fetch the next step's A fragments
+            load_w(ks + kDW, ru[d]);
+            load_a(ks + 1, anext);
+            const uint16_t* bbase =
+                wl + (d & 1) * S::kBuf + (lane & 15) * kLRow + 8 * (lane >> 4);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const bf16x8 bfr =
+                        *reinterpret_cast<const bf16x8*>(bbase + 16 * j * kLRow + 32 * h);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[h][i], bfr,
+                                                                            acc[i][j], 0, 0, 0);
+                }
+            }
+            store_w(ks + 1, ru[(d + 1) % kDW], wl + ((d + 1) & 1) * S::kBuf);
+            __syncthreads();
+        }
+    }
+
+    // D[i][j]: lane holds rows 4*(lane/16) + r, column lane%16 of each sub-tile.
+    const int64_t nend = min(n0 + p.stride, p.n);
+    float* out = p.splits == 1 ? p.c : p.c + (int64_t)split * p.m * p.n;
+    const int64_t ld = p.splits == 1 ? p.ldc : p.n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int64_t col = n0 + 16 * j + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + 32 * wv + 16 * mi + 4 * (lane >> 4) + r;
-                if (row < m && col < n) c[row * ldc + col] = acc[mi][nj][r];
+                const int64_t row = m0 + 16 * i + 4 * (lane >> 4) + r;
+                if (row < p.m && col < nend) out[row * ld + col] = acc[i][j][r];
             }
         }
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int64_t m, int64_t n,
+                                                            float* __restrict__ c, int64_t ldc) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m * n) return;
+    const int64_t row = i / n, col = i % n;
+    float s = 0.f;
+    for (int q = 0; q < splits; ++q) s += part[q * m * n + i];
+    c[row * ldc + col] = s;
+}
+
+// Tile plan: waves per workgroup WV (rows 64*WV), column-tile width BN = 16*NT
+// and stride, K splits.  The estimate is the MFMA time of the busiest compute
+// unit (workgroups run in rounds over 256 units, each holding two waves per
+// SIMD) plus the fp32 partial-sum traffic of a split.
+struct Plan {
+    int wv, nt, stride, splits, tiles_m, tiles_n;
+};
+
+constexpr int kCUs = 256;
+
+Plan plan_for(int64_t m, int64_t n, int64_t k) {
+    const int64_t ksteps = kpad(k) / kBK;
+    Plan best{4, 4, 64, 1, 1, 1};
+    double best_t = 1e300;
+    int64_t best_wgs = 0;
+    const int wvs[] = {8, 4};
+    const int nts[] = {6, 5, 4, 3, 2, 1};
+    for (int wv : wvs) {
+        const int64_t tiles_m = (m + 64 * wv - 1) / (64 * wv);
+        const int64_t slots = (int64_t)kCUs * (8 / wv);   // resident workgroups
+        for (int nt : nts) {
+            const int bn = 16 * nt;
+            for (int stride = bn; stride >= bn / 2 && stride > 0; stride -= 4) {
+                const int64_t tn = (n + stride - 1) / stride;
+                for (int s = 1; s <= 8; s *= 2) {
+                    if (s > 1 && ksteps / s < 8) break;
+                    const int64_t kper = (ksteps + s - 1) / s;
+                    const int64_t wgs = tiles_m * tn * s;
+                    const int64_t rounds = (wgs + slots - 1) / slots;
+                    // cycles: 2048 MACs per CU-cycle at ~50% of peak; 2500 bytes per
+                    // cycle of memory for the partials (written and read back)
+                    double t = (double)rounds * (8 / wv) * (64.0 * wv) * bn * (kper * kBK) / 1024.0;
+                    if (s > 1) t += (double)s * m * n * 8.0 / 2500.0;
+                    if (t < best_t * 0.999 || (t <= best_t * 1.001 && wgs < best_wgs)) {
+                        best_t = t;
+                        best_wgs = wgs;
+                        best = Plan{wv, nt, stride, s, (int)tiles_m, (int)tn};
+                    }
+                }
+            }
+        }
+    }
+    return best;
+}
+
+template <int FMT, int WV, int NT>
+hipError_t launch_main(const GemmArgs& a, hipStream_t s) {
+    using S = GemmShape<WV, NT>;
+    const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n * a.splits);
+    hipLaunchKernelGGL((gemm_kernel<FMT, WV, NT>), dim3(grid), dim3(S::THREADS), S::kLds, s, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int WV>
+hipError_t launch_nt(const GemmArgs& a, int nt, hipStream_t s) {
+    switch (nt) {
+        case 6: return launch_main<FMT, WV, 6>(a, s);
+        case 5: return launch_main<FMT, WV, 5>(a, s);
+        case 4: return launch_main<FMT, WV, 4>(a, s);
+        case 3: return launch_main<FMT, WV, 3>(a, s);
+        case 2: return launch_main<FMT, WV, 2>(a, s);
+        default: return launch_main<FMT, WV, 1>(a, s);
+    }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const GemmArgs& a, const Plan& pl, hipStream_t s) {
+    return pl.wv == 8 ? launch_nt<FMT, 8>(a, pl.nt, s) : launch_nt<FMT, 4>(a, pl.nt, s);
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(int type, int64_t m, int64_t n, int64_t k) {
     (void)type;
-    (void)n;
-    return (size_t)m * (size_t)kpad(k) * 2 + 256;
+    const Plan pl = plan_for(m, n, k);
+    size_t bytes = ((size_t)mpad(m) * (size_t)kpad(k) * 2 + 255) / 256 * 256;
+    if (pl.splits > 1) bytes += (size_t)pl.splits * (size_t)m * (size_t)n * 4;
+    return bytes + 256;
 }
 
 hipError_t launch_gemm(int type, const uint8_t* w, int64_t n, int64_t k, const float* a,
                        int64_t lda, int64_t m, float* c, int64_t ldc, void* ws, hipStream_t s) {
     const int64_t kp = kpad(k);
     uint16_t* abf = static_cast<uint16_t*>(ws);
-    const int64_t total = m * (kp / 4);
+    const int64_t total = mpad(m) * (kp / 4);
     hipLaunchKernelGGL(prep_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,
                        lda, m, k, kp, abf);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t rb = row_bytes(type, k);
-    constexpr int NT = 8;
-    dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)), (unsigned)((m + kBM - 1) / kBM));
-    if (type == kQ4_K)
-        hipLaunchKernelGGL((gemm_kernel<kQ4_K, NT>), grid, dim3(256), 0, s, w, n, k, rb, abf, kp, m,
-                           c, ldc);
-    else
-        hipLaunchKernelGGL((gemm_kernel<kQ8_0, NT>), grid, dim3(256), 0, s, w, n, k, rb, abf, kp, m,
-                           c, ldc);
+    const Plan pl = plan_for(m, n, k);
+    GemmArgs g;
+    g.w = w;
+    g.abf = abf;
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                           ((size_t)mpad(m) * (size_t)kp * 2 + 255) / 256 * 256);
+    g.c = pl.splits == 1 ? c : part;
+    g.n = n;
+    g.k = k;
+    g.rb = row_bytes(type, k);
+    g.kp = kp;
+    g.m = m;
+    g.ldc = ldc;
+    g.stride = pl.stride;
+    g.tiles_m = pl.tiles_m;
+    g.tiles_n = pl.tiles_n;
+    g.splits = pl.splits;
+    const int ksteps = (int)(kp / kBK);
+    g.ksteps_per_split = (ksteps + pl.splits - 1) / pl.splits;
+    err = type == kQ4_K ? launch_fmt<kQ4_K>(g, pl, s) : launch_fmt<kQ8_0>(g, pl, s);
+    if (err != hipSuccess || pl.splits == 1) return err;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((m * n + 255) / 256)), dim3(256), 0, s,
+                       part, pl.splits, m, n, c, ldc);
     return hipGetLastError();
 }
 
