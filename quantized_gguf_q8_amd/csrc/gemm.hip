@@ -66,25 +66,33 @@ __host__ __device__ inline int64_t frag_offset(int64_t st, int64_t g, int h, int
     return (((st * groups + g) * 2 + h) * 64 + l) * 16;
 }
 
+// One thread per 16-byte fragment piece, in output order: a wave writes 1 KiB
+// contiguously and reads 16 rows x 128 contiguous bytes.
 __global__ __launch_bounds__(256) void prep_bf16_kernel(const float* __restrict__ a, int64_t lda,
                                                         int64_t m, int64_t k, int64_t kp,
                                                         uint16_t* __restrict__ out) {
-    const int64_t q = kp / 4;
-    const int64_t m16 = mpad(m);
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= m16 * q) return;
-    const int64_t row = i / q;
-    const int64_t col = (i % q) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < m && col < k) v = *reinterpret_cast<const float4*>(a + row * lda + col);
-    uint2 o;
-    o.x = cvt_bf16x2(v.x, v.y);
-    o.y = cvt_bf16x2(v.z, v.w);
-    // element (row, col): step col/64, half (col%64)/32, lane row%16 + 16*((col%32)/8)
-    const int cc = (int)(col % kBK);
-    const int lane = (int)(row % 16) + 16 * ((cc % 32) / 8);
-    const int64_t off = frag_offset(col / kBK, row / 16, cc / 32, lane, m16 / 16) + 2 * (cc % 8);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(out) + off) = o;
+    const int64_t groups = mpad(m) / 16;
+    const int64_t pieces = groups * 16 * kp / 8;
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= pieces) return;
+    const int l = (int)(p % 64);
+    const int h = (int)((p / 64) % 2);
+    const int64_t g = (p / 128) % groups;
+    const int64_t st = p / 128 / groups;
+    const int64_t row = g * 16 + l % 16;
+    const int64_t col = st * kBK + 32 * h + 8 * (l / 16);
+    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+    if (row < m && col < k) {   // k is a multiple of 32
+        const float4* src = reinterpret_cast<const float4*>(a + row * lda + col);
+        v0 = src[0];
+        v1 = src[1];
+    }
+    uint4 o;
+    o.x = cvt_bf16x2(v0.x, v0.y);
+    o.y = cvt_bf16x2(v0.z, v0.w);
+    o.z = cvt_bf16x2(v1.x, v1.y);
+    o.w = cvt_bf16x2(v1.z, v1.w);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(out) + frag_offset(st, g, h, l, groups)) = o;
 }
 
 // One decode unit = 16 weights of one W row in the current step.
@@ -446,7 +454,7 @@ hipError_t launch_gemm(int type, const uint8_t* w, int64_t n, int64_t k, const f
                        int64_t lda, int64_t m, float* c, int64_t ldc, void* ws, hipStream_t s) {
     const int64_t kp = kpad(k);
     uint16_t* abf = static_cast<uint16_t*>(ws);
-    const int64_t total = mpad(m) * (kp / 4);
+    const int64_t total = mpad(m) * (kp / 8);
     hipLaunchKernelGGL(prep_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,
                        lda, m, k, kp, abf);
     hipError_t err = hipGetLastError();
