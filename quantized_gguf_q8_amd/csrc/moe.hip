@@ -12,16 +12,19 @@
 // selected set.
 //
 // Expert layer, four launches on the caller's stream:
-//   1. group   : one workgroup sorts the T*top_k (token, slot) pairs by expert
-//                (stable), giving per-expert pair lists and the ascending list
-//                of experts that received any pair.
-//   2. gate/up : per (selected expert, row tile): the gate and up rows of that
-//                expert against every token routed to it (gemv_tile with two
-//                matrices), epilogue h = silu(g) * u.
+//   1. group   : a stable counting sort of the T*top_k (token, slot) pairs by
+//                expert, giving per-expert pair lists and the ascending list of
+//                experts that received any pair.  Up to 256 pairs (decode
+//                batches) every workgroup of the next two stages redoes it in
+//                LDS, which is cheaper than a launch; beyond that one workgroup
+//                writes the lists to the workspace first.
+//   2. gate/up : per (selected expert, row tile): the same rows of that expert's
+//                gate and up matrices against every token routed to it,
+//                epilogue h = silu(g) * u.
 //   3. down    : per (selected expert, row tile): d = Wd h for each of its pairs.
 //   4. combine : y[t] = sum_s probs[t][s] * d_(t,s) in slot order.
-// Only the selected experts' bytes are read, each once per launch (tokens are
-// batched per expert), and nothing is accumulated with atomics.
+// Only the selected experts' bytes are read, once per group of up to 16 tokens
+// routed to the expert, and nothing is accumulated with atomics.
 #include "gemv_core.h"
 #include "ggq_launch.h"
 
@@ -33,33 +36,53 @@ constexpr int kMaxTopK = 32;
 
 // ---------------------------------------------------------------- router ----
 // One wave per expert, all tokens.  logits[t][e] = sum_h wr[e][h] x[t][h].
+// Each 16-byte piece of the router row is loaded once and applied to up to 4
+// tokens (token groups spread over the grid's second dimension); per token a
+// lane keeps four component sums, combined pairwise, and the wave's lanes are
+// summed by a fixed butterfly.
 __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restrict__ wr,
                                                             int64_t e, int64_t h,
                                                             const float* __restrict__ x,
                                                             int64_t t, float* __restrict__ logits) {
+    constexpr int kTok = 4;
     const int lane = threadIdx.x & 63;
     const int64_t ei = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (ei >= e) return;
     const float4* w4 = reinterpret_cast<const float4*>(wr + ei * h);
     const int64_t h4 = h / 4;
-    for (int64_t ti = 0; ti < t; ++ti) {
-        const float4* x4 = reinterpret_cast<const float4*>(x + ti * h);
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
+    // token groups of kTok are spread over blockIdx.y (and looped beyond that)
+    for (int64_t t0 = (int64_t)blockIdx.y * kTok; t0 < t; t0 += (int64_t)gridDim.y * kTok) {
+        const int nt = (int)(t - t0 < kTok ? t - t0 : kTok);
+        float p[kTok][4];
+#pragma unroll
+        for (int j = 0; j < kTok; ++j) p[j][0] = p[j][1] = p[j][2] = p[j][3] = 0.f;
         for (int64_t i = lane; i < h4; i += 64) {
-            float4 a = w4[i];
-            float4 b = x4[i];
-            p[0] += a.x * b.x;
-            p[1] += a.y * b.y;
-            p[2] += a.z * b.z;
-            p[3] += a.w * b.w;
+            const float4 a = w4[i];
+#pragma unroll
+            for (int j = 0; j < kTok; ++j) {
+                if (j < nt) {
+                    const float4 b = reinterpret_cast<const float4*>(x + (t0 + j) * h)[i];
+                    p[j][0] += a.x * b.x;
+                    p[j][1] += a.y * b.y;
+                    p[j][2] += a.z * b.z;
+                    p[j][3] += a.w * b.w;
+                }
+            }
         }
-        float s = wave_sum((p[0] + p[1]) + (p[2] + p[3]));
-        if (lane == 0) logits[ti * e + ei] = s;
+#pragma unroll
+        for (int j = 0; j < kTok; ++j) {
+            if (j < nt) {
+                const float sum = wave_sum((p[j][0] + p[j][1]) + (p[j][2] + p[j][3]));
+                if (lane == 0) logits[(t0 + j) * e + ei] = sum;
+            }
+        }
     }
 }
 
 // One wave per token: top_k rounds of a wave-wide argmax (ties -> lower index),
 // then exp(l - l_max) over the selected logits, normalised in rank order.
+// kPer logits per lane: E <= 64*kPer.
+template <int kPer>
 __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restrict__ logits,
                                                           int64_t e, int top_k,
                                                           int32_t* __restrict__ idx,
@@ -67,7 +90,6 @@ __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restric
     const int64_t ti = blockIdx.x;
     const int lane = threadIdx.x;
     const float* l = logits + ti * e;
-    constexpr int kPer = 16;  // E <= 1024
     float v[kPer];
     uint32_t taken = 0;
 #pragma unroll
@@ -202,76 +224,377 @@ __global__ __launch_bounds__(256) void group_kernel(const int32_t* __restrict__ 
 }
 
 // ------------------------------------------------------- expert GEMVs ----
-template <int NB>
-struct HEpi {
-    float* hbuf;
-    int64_t f;
-    const int32_t* pairs;  // this group's pair ids
-    __device__ void operator()(int b, int64_t r, const float (&v)[2]) const {
-        float g = v[0], u = v[1];
-        float silu = g / (1.0f + expf(-g));
-        hbuf[(int64_t)pairs[b] * f + r] = silu * u;
-    }
+// Both expert stages are persistent streaming GEMVs over a device-side work
+// list (the active experts are known only after routing).  A tile is ROWS rows
+// of one selected expert (of both its gate and up matrices in stage 1); a unit
+// is one K chunk of a tile for one group of up to NB of the expert's tokens.  A
+// workgroup takes tiles blockIdx.x, +gridDim.x, ... and walks each tile's units
+// in order; while it computes one unit from LDS, the 16-byte loads of the next
+// (weight rows, coalesced, and the gathered activation chunk) are in flight.
+// The thread layout and the per-thread decode are those of the decode GEMV:
+// thread (row rl, slice s) owns 64 weights of its row per chunk, decodes them
+// once and applies them to every token of the group; a row's slices sit in one
+// wave and are combined by a fixed butterfly.
+template <int FMT, int NB, int ROWS, int NMAT>
+struct MoeCfg {
+    using Base = GemvCfg<FMT, NB, ROWS, NMAT>;
+    static constexpr int SL = Base::SL;
+    static constexpr int KC = Base::KC;
+    static constexpr int CRB = Base::CRB;
+    static constexpr int WRS = Base::WRS;
+    static constexpr int XSS = Base::XSS;
+    static constexpr int XBS = Base::XBS;
+    static constexpr int PPR = CRB / 16;               // 16-byte pieces per row chunk
+    static constexpr int MPIECES = ROWS * PPR;          // per matrix
+    static constexpr int WPIECES = NMAT * MPIECES;
+    static constexpr int WP = (WPIECES + 255) / 256;
+    static constexpr int XPIECES = NB * KC / 4;
+    static constexpr int XP = (XPIECES + 255) / 256;
+    static constexpr int kWBytes = NMAT * ROWS * WRS;
+    static constexpr int kXBytes = NB * XBS * 4;
+    static constexpr int kSumBytes = FMT == kQ4_K ? NB * SL * 2 * 4 : 0;
+    static constexpr int kXBuf = kXBytes + kSumBytes;
+    static constexpr int kLds = 2 * kWBytes + 2 * kXBuf;
+    // a wave's 64 consecutive weight pieces come from one matrix
+    static_assert(MPIECES % 64 == 0, "matrix pieces must be whole waves");
 };
 
-template <int NB>
-struct DEpi {
-    float* dbuf;
-    int64_t h;
-    const int32_t* pairs;
-    __device__ void operator()(int b, int64_t r, const float (&v)[1]) const {
-        dbuf[(int64_t)pairs[b] * h + r] = v[0];
-    }
+struct MoeStage {
+    const uint8_t* w[2];   // expert-stacked matrices [E][n][rb] (stage 1: gate, up)
+    int64_t n, rb;         // rows per expert matrix, bytes per row
+    int32_t k;             // weights per row
+    int32_t nchunk;        // K chunks per row
+    int32_t tiles;         // row tiles per expert
+    const float* x;        // activation rows, k floats each
+    int64_t xrows;
+    int32_t xdiv;          // activation row of pair p: p / xdiv
+    float* y;              // output row of pair p: y + p * n
+    MoeWs ws;              // global lists (written by group_kernel) ...
+    const int32_t* idx;    // ... or, with inline_group, rebuilt in LDS from idx
+    int32_t p, e;          // pairs, experts
+    int32_t inline_group;
 };
 
-template <int FMT, int NB, int ROWS>
-__global__ __launch_bounds__(256) void expert_gate_up_kernel(const uint8_t* __restrict__ wg,
-                                                             const uint8_t* __restrict__ wu,
-                                                             int64_t hdim, int64_t f,
-                                                             const float* __restrict__ x,
-                                                             int top_k, MoeWs ws) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    const int a = blockIdx.y;
-    if (a >= ws.nact[0]) return;
-    const int ex = ws.active[a];
-    const int cnt = ws.cnt[ex];
-    const int32_t* pairs = ws.list + ws.off[ex];
-    const int64_t rb = row_bytes_dev<FMT>(hdim);
-    const uint8_t* wm[2] = {wg + (int64_t)ex * f * rb, wu + (int64_t)ex * f * rb};
-    for (int g0 = 0; g0 < cnt; g0 += NB) {
-        const int batch = min(NB, cnt - g0);
-        const float* xr[NB];
+// Pair lists by expert: counts, list offsets, ascending active experts, and the
+// pair ids sorted by (expert, pair).  In LDS or in the workspace.
+struct MoeLists {
+    const int32_t* cnt;
+    const int32_t* off;
+    const int32_t* active;
+    const int32_t* list;
+    const int32_t* xrow;   // activation row of each list entry (LDS lists only)
+    int nact;
+};
+
+constexpr int kInlinePairs = 256;   // up to this many pairs are grouped in LDS
+
+__host__ __device__ inline int inline_group_bytes(int64_t e, int64_t p) {
+    return (int)((3 * e + 1 + 3 * p) * 4);
+}
+
+// Stable counting sort of the p pairs by expert in LDS, by one workgroup of 256
+// threads; the same lists group_kernel writes to the workspace.
+__device__ __forceinline__ MoeLists group_in_lds(const int32_t* __restrict__ idx, int p, int e,
+                                                 int xdiv, int32_t* g) {
+    int32_t* cnt = g;
+    int32_t* off = g + e;
+    int32_t* act = g + 2 * e;
+    int32_t* nact = g + 3 * e;
+    int32_t* list = g + 3 * e + 1;
+    int32_t* ix = list + p;
+    int32_t* xr = ix + p;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < e; i += 256) cnt[i] = 0;
+    for (int i = tid; i < p; i += 256) {
+        int32_t ex = idx[i];
+        ix[i] = (ex < 0 || ex >= e) ? 0 : ex;
+    }
+    __syncthreads();
+    for (int i = tid; i < p; i += 256) atomicAdd(&cnt[ix[i]], 1);
+    __syncthreads();
+    if (tid < 64) {
+        // lane l owns experts [l*per, l*per + per): exclusive scans of the pair
+        // counts and of the active flags across the wave
+        const int lane = tid;
+        const int per = (e + 63) / 64;
+        const int b0 = lane * per;
+        int sp = 0, sa = 0;
+        for (int i = b0; i < min(b0 + per, e); ++i) {
+            sp += cnt[i];
+            sa += cnt[i] > 0;
+        }
+        int ip = sp, ia = sa;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            xr[b] = x + (int64_t)(pairs[g0 + (b < batch ? b : 0)] / top_k) * hdim;
-        HEpi<NB> epi{ws.hbuf, f, pairs + g0};
-        gemv_tile<FMT, NB, ROWS, 2>(lds, wm, f, (int)hdim, rb, xr, batch,
-                                    (int64_t)blockIdx.x * ROWS, epi);
-        __syncthreads();
+        for (int d = 1; d < 64; d <<= 1) {
+            const int tp = __shfl_up(ip, d, 64);
+            const int ta = __shfl_up(ia, d, 64);
+            if (lane >= d) {
+                ip += tp;
+                ia += ta;
+            }
+        }
+        int run = ip - sp, na = ia - sa;
+        for (int i = b0; i < min(b0 + per, e); ++i) {
+            off[i] = run;
+            if (cnt[i] > 0) act[na++] = i;
+            run += cnt[i];
+        }
+        if (lane == 63) nact[0] = ia;
+    }
+    __syncthreads();
+    for (int i = tid; i < p; i += 256) {
+        const int ex = ix[i];
+        int rank = 0;
+        for (int j = 0; j < i; ++j) rank += ix[j] == ex;
+        list[off[ex] + rank] = i;
+        xr[off[ex] + rank] = i / xdiv;
+    }
+    __syncthreads();
+    return MoeLists{cnt, off, act, list, xr, nact[0]};
+}
+
+struct MoeUnit {
+    int tile;
+    int e;
+    int64_t r0;
+    int g0;      // first token of the group within the expert's list
+    int cnt;     // tokens routed to the expert
+    int chunk;
+    const int32_t* pairs;
+    const int32_t* xrows;  // activation row per pair, or null: pair / xdiv
+};
+
+template <int ROWS>
+__device__ __forceinline__ bool moe_locate(const MoeStage& st, const MoeLists& L, int tile,
+                                           int total, MoeUnit& u) {
+    if (tile >= total) return false;
+    u.tile = tile;
+    u.e = L.active[tile / st.tiles];
+    u.r0 = (int64_t)(tile % st.tiles) * ROWS;
+    u.g0 = 0;
+    u.cnt = L.cnt[u.e];
+    u.chunk = 0;
+    u.pairs = L.list + L.off[u.e];
+    u.xrows = L.xrow ? L.xrow + L.off[u.e] : nullptr;
+    return true;
+}
+
+template <int NB, int ROWS>
+__device__ __forceinline__ bool moe_next(const MoeStage& st, const MoeLists& L, const MoeUnit& p,
+                                         int total, MoeUnit& q) {
+    q = p;
+    if (p.chunk + 1 < st.nchunk) {
+        q.chunk = p.chunk + 1;
+        return true;
+    }
+    if (p.g0 + NB < p.cnt) {
+        q.g0 = p.g0 + NB;
+        q.chunk = 0;
+        return true;
+    }
+    return moe_locate<ROWS>(st, L, p.tile + (int)gridDim.x, total, q);
+}
+
+template <int FMT, int NB, int ROWS, int NMAT>
+struct MoePrefetch {
+    using C = MoeCfg<FMT, NB, ROWS, NMAT>;
+    uint4 w[C::WP];
+    uint4 x[C::XP];
+
+    __device__ __forceinline__ void load_w(const MoeStage& st, const MoeUnit& u, int tid,
+                                           int wave) {
+        const uint32_t bytes = (uint32_t)(st.n * st.rb);
+        const __amdgpu_buffer_rsrc_t r0 = make_rsrc(st.w[0] + (int64_t)u.e * st.n * st.rb, bytes);
+        const __amdgpu_buffer_rsrc_t r1 =
+            make_rsrc(st.w[NMAT - 1] + (int64_t)u.e * st.n * st.rb, bytes);
+        const uint32_t cb0 = (uint32_t)u.chunk * C::CRB;
+        const uint32_t rb = (uint32_t)st.rb;
+#pragma unroll
+        for (int i = 0; i < C::WP; ++i) {
+            const int q = tid + 256 * i;
+            const int m = (64 * wave + 256 * i) / C::MPIECES;   // uniform per wave
+            const int qm = q - m * C::MPIECES;
+            const uint32_t row = (uint32_t)u.r0 + (uint32_t)(qm / C::PPR);
+            const uint32_t off = (uint32_t)(qm % C::PPR) * 16;
+            const bool ok = q < C::WPIECES && row < (uint32_t)st.n && cb0 + off < rb;
+            w[i] = buf_load16<true>(m ? r1 : r0, ok ? row * rb + cb0 + off : kOob);
+        }
+    }
+
+    __device__ __forceinline__ void load_x(const MoeStage& st, const MoeUnit& u, int tid) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(st.x, (uint32_t)(st.xrows * st.k * 4));
+        const int k0 = u.chunk * C::KC;
+        const int batch = min(NB, u.cnt - u.g0);
+#pragma unroll
+        for (int i = 0; i < C::XP; ++i) {
+            const int q = tid + 256 * i;
+            const int b = q / (C::KC / 4);
+            const int pos = (q % (C::KC / 4)) * 4;
+            if (b >= batch) continue;   // uniform per wave: a wave's pieces share b
+            uint32_t off = kOob;
+            if (q < C::XPIECES && k0 + pos < st.k) {
+                const int64_t xr =
+                    u.xrows ? u.xrows[u.g0 + b] : u.pairs[u.g0 + b] / st.xdiv;
+                off = (uint32_t)((xr * st.k + k0 + pos) * 4);
+            }
+            x[i] = buf_load16<false>(r, off);
+        }
+    }
+
+    __device__ __forceinline__ void store_w(uint8_t* lw, int tid) const {
+#pragma unroll
+        for (int i = 0; i < C::WP; ++i) {
+            const int q = tid + 256 * i;
+            if (q < C::WPIECES) {
+                const int pr = q / C::PPR;   // row within the NMAT*ROWS stacked tile
+                const int off = (q % C::PPR) * 16;
+                *reinterpret_cast<uint4*>(lw + pr * C::WRS + off) = w[i];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store_x(uint8_t* xbuf, int tid, int batch) const {
+        float* lx = reinterpret_cast<float*>(xbuf);
+        float* lsum = reinterpret_cast<float*>(xbuf + C::kXBytes);
+#pragma unroll
+        for (int i = 0; i < C::XP; ++i) {
+            const int q = tid + 256 * i;
+            const int b = q / (C::KC / 4);
+            // whole waves only (KC/4 is a multiple of 64); rows past the group's
+            // tokens are never read
+            if ((C::XPIECES % 256 == 0 || q < C::XPIECES) && b < batch) {
+                const int pos = (q % (C::KC / 4)) * 4;
+                const float4 v = __builtin_bit_cast(float4, x[i]);
+                *reinterpret_cast<float4*>(lx + b * C::XBS + (pos >> 6) * C::XSS + (pos & 63)) = v;
+                if constexpr (FMT == kQ4_K) {
+                    float t = (v.x + v.y) + (v.z + v.w);
+                    t += __shfl_xor(t, 1, 64);
+                    t += __shfl_xor(t, 2, 64);
+                    t += __shfl_xor(t, 4, 64);
+                    if ((q & 7) == 0) lsum[(b * C::SL + (pos >> 6)) * 2 + ((pos >> 5) & 1)] = t;
+                }
+            }
+        }
+    }
+};
+
+template <int FMT, int NB, int ROWS, int NMAT>
+__device__ __forceinline__ void moe_compute(const MoeStage& st, const MoeUnit& u,
+                                            const uint8_t* lw, const uint8_t* xbuf, int s, int rl,
+                                            float (&acc)[NMAT][NB]) {
+    using C = MoeCfg<FMT, NB, ROWS, NMAT>;
+    constexpr int SL = C::SL;
+    const float* lx = reinterpret_cast<const float*>(xbuf);
+    const float* lsum = reinterpret_cast<const float*>(xbuf + C::kXBytes);
+    const int k0 = u.chunk * C::KC;
+    const int batch = min(NB, u.cnt - u.g0);
+    if (u.r0 + rl < st.n && k0 + s * 64 < st.k) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            float f0[32], f1[32];
+            float sa0, sa1, mb0, mb1;
+            decode_unit<FMT>(lw + (m * ROWS + rl) * C::WRS, s, f0, f1, sa0, sa1, mb0, mb1);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b < batch) {
+                    const float4* xv = reinterpret_cast<const float4*>(lx + b * C::XBS + s * C::XSS);
+                    float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        float4 a = xv[i];
+                        float4 e = xv[8 + i];
+                        p0[i & 3] += f0[4 * i] * a.x + f0[4 * i + 1] * a.y + f0[4 * i + 2] * a.z +
+                                     f0[4 * i + 3] * a.w;
+                        p1[i & 3] += f1[4 * i] * e.x + f1[4 * i + 1] * e.y + f1[4 * i + 2] * e.z +
+                                     f1[4 * i + 3] * e.w;
+                    }
+                    float t = sa0 * ((p0[0] + p0[1]) + (p0[2] + p0[3])) +
+                              sa1 * ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+                    if constexpr (FMT == kQ4_K) {
+                        const float* xs = lsum + (b * SL + s) * 2;
+                        t -= mb0 * xs[0] + mb1 * xs[1];
+                    }
+                    acc[m][b] += t;
+                }
+            }
+        }
+    }
+    if (u.chunk == st.nchunk - 1) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int o = 1; o < SL; o <<= 1) acc[m][b] += __shfl_xor(acc[m][b], o, 64);
+        if (s == 0 && u.r0 + rl < st.n) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b < batch) {
+                    float v = acc[0][b];
+                    if constexpr (NMAT == 2) {   // h = silu(gate) * up
+                        const float g = acc[0][b];
+                        v = g / (1.0f + expf(-g)) * acc[1][b];
+                    }
+                    st.y[(int64_t)u.pairs[u.g0 + b] * st.n + u.r0 + rl] = v;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[m][b] = 0.f;
     }
 }
 
-template <int FMT, int NB, int ROWS>
-__global__ __launch_bounds__(256) void expert_down_kernel(const uint8_t* __restrict__ wd,
-                                                          int64_t hdim, int64_t f, MoeWs ws) {
+template <int FMT, int NB, int ROWS, int NMAT>
+__global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
+    using C = MoeCfg<FMT, NB, ROWS, NMAT>;
     extern __shared__ __align__(16) uint8_t lds[];
-    const int a = blockIdx.y;
-    if (a >= ws.nact[0]) return;
-    const int ex = ws.active[a];
-    const int cnt = ws.cnt[ex];
-    const int32_t* pairs = ws.list + ws.off[ex];
-    const int64_t rb = row_bytes_dev<FMT>(f);
-    const uint8_t* wm[1] = {wd + (int64_t)ex * hdim * rb};
-    for (int g0 = 0; g0 < cnt; g0 += NB) {
-        const int batch = min(NB, cnt - g0);
-        const float* xr[NB];
+    uint8_t* lw0 = lds;
+    uint8_t* lx0 = lds + 2 * C::kWBytes;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = tid % C::SL;
+    const int rl = tid / C::SL;
+    MoeLists L;
+    if (st.inline_group) {
+        L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lds + C::kLds));
+    } else {
+        L = MoeLists{st.ws.cnt, st.ws.off, st.ws.active, st.ws.list, nullptr, st.ws.nact[0]};
+    }
+    const int total = L.nact * st.tiles;
+
+    MoeUnit cur;
+    if (!moe_locate<ROWS>(st, L, blockIdx.x, total, cur)) return;
+    MoePrefetch<FMT, NB, ROWS, NMAT> pf;
+    pf.load_w(st, cur, tid, wave);
+    pf.load_x(st, cur, tid);
+    pf.store_w(lw0, tid);
+    pf.store_x(lx0, tid, min(NB, cur.cnt - cur.g0));
+    __syncthreads();
+
+    float acc[NMAT][NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            xr[b] = ws.hbuf + (int64_t)pairs[g0 + (b < batch ? b : 0)] * f;
-        DEpi<NB> epi{ws.dbuf, hdim, pairs + g0};
-        gemv_tile<FMT, NB, ROWS, 1>(lds, wm, hdim, (int)f, rb, xr, batch,
-                                    (int64_t)blockIdx.x * ROWS, epi);
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[m][b] = 0.f;
+
+    int buf = 0;
+    for (;;) {
+        MoeUnit nxt;
+        const bool more = moe_next<NB, ROWS>(st, L, cur, total, nxt);
+        if (more) {
+            pf.load_w(st, nxt, tid, wave);
+            pf.load_x(st, nxt, tid);
+        }
+        moe_compute<FMT, NB, ROWS, NMAT>(st, cur, lw0 + buf * C::kWBytes, lx0 + buf * C::kXBuf, s,
+                                         rl, acc);
+        if (!more) break;
+        buf ^= 1;
+        pf.store_w(lw0 + buf * C::kWBytes, tid);
+        pf.store_x(lx0 + buf * C::kXBuf, tid, min(NB, nxt.cnt - nxt.g0));
         __syncthreads();
+        cur = nxt;
     }
 }
 
@@ -295,50 +618,120 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     y[ti * hdim + r] = acc;
 }
 
+int moe_device_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int FMT, int NB, int ROWS, int NMAT>
+hipError_t launch_stage(MoeStage st, int64_t slots, hipStream_t s) {
+    using C = MoeCfg<FMT, NB, ROWS, NMAT>;
+    const size_t lds = C::kLds + (st.inline_group ? inline_group_bytes(st.e, st.p) : 0);
+    // resident workgroups per compute unit for this LDS size (cached for the
+    // last size asked)
+    static size_t per_cu_lds = 0;
+    static int per_cu = 0;
+    if (per_cu_lds != lds) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_stream_kernel<FMT, NB, ROWS, NMAT>,
+                                                         256, lds) != hipSuccess || v <= 0)
+            v = 1;
+        per_cu = v;
+        per_cu_lds = lds;
+    }
+    st.nchunk = (st.k + C::KC - 1) / C::KC;
+    st.tiles = (int32_t)((st.n + ROWS - 1) / ROWS);
+    const int64_t most = slots * st.tiles;
+    const int64_t cap = (int64_t)per_cu * moe_device_cus();
+    const unsigned grid = (unsigned)(most < cap ? most : cap);
+    hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT>), dim3(grid), dim3(256), lds, s,
+                       st);
+    return hipGetLastError();
+}
+
+// Rows per tile: the largest of 64/32/16 (at least 2*NB) that still gives every
+// compute unit two tiles when `slots` experts are active.
+template <int FMT, int NB, int NMAT>
+hipError_t launch_stage_rows(const MoeStage& st, int64_t slots, hipStream_t s) {
+    const int64_t want = 2 * (int64_t)moe_device_cus();
+    int rows = 64;
+    while (rows > 16 && rows / 2 >= 2 * NB && slots * ((st.n + rows - 1) / rows) < want) rows /= 2;
+    if (rows == 64) return launch_stage<FMT, NB, 64, NMAT>(st, slots, s);
+    if constexpr (2 * NB <= 32)
+        if (rows == 32) return launch_stage<FMT, NB, 32, NMAT>(st, slots, s);
+    if constexpr (2 * NB <= 16)
+        if (rows == 16) return launch_stage<FMT, NB, 16, NMAT>(st, slots, s);
+    return launch_stage<FMT, NB, 32, NMAT>(st, slots, s);
+}
+
 template <int FMT, int NB>
 hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, int64_t e,
-                          int64_t hdim, int64_t f, const float* x, int64_t p, int top_k,
-                          const MoeWs& ws, hipStream_t s) {
-    const unsigned max_act = (unsigned)(p < e ? p : e);
-    {
-        const int rows = gemv_rows_for(NB, hdim);
-        dim3 grid((unsigned)((f + rows - 1) / rows), max_act);
-#define GGQ_GU(R)                                                                               \
-    hipLaunchKernelGGL((expert_gate_up_kernel<FMT, NB, R>), grid, dim3(256),                    \
-                       (GemvCfg<FMT, NB, R, 2>::kLds), s, wg, wu, hdim, f, x, top_k, ws)
-        if (rows == 8) GGQ_GU(8);
-        else if (rows == 16) GGQ_GU(16);
-        else if (rows == 32) GGQ_GU(32);
-        else GGQ_GU(64);
-#undef GGQ_GU
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
-    {
-        const int rows = gemv_rows_for(NB, f);
-        dim3 grid((unsigned)((hdim + rows - 1) / rows), max_act);
-#define GGQ_DN(R)                                                                               \
-    hipLaunchKernelGGL((expert_down_kernel<FMT, NB, R>), grid, dim3(256),                       \
-                       (GemvCfg<FMT, NB, R, 1>::kLds), s, wd, hdim, f, ws)
-        if (rows == 8) GGQ_DN(8);
-        else if (rows == 16) GGQ_DN(16);
-        else if (rows == 32) GGQ_DN(32);
-        else GGQ_DN(64);
-#undef GGQ_DN
-        return hipGetLastError();
-    }
+                          int64_t hdim, int64_t f, const float* x, int64_t t, int top_k,
+                          const int32_t* idx, const MoeWs& ws, hipStream_t s) {
+    const int64_t p = t * top_k;
+    const int64_t slots = p < e ? p : e;
+    const bool inl = p <= kInlinePairs;
+    MoeStage a{};
+    a.idx = idx;
+    a.p = (int32_t)p;
+    a.e = (int32_t)e;
+    a.inline_group = inl;
+    a.w[0] = wg;
+    a.w[1] = wu;
+    a.n = f;
+    a.rb = row_bytes(FMT, hdim);
+    a.k = (int32_t)hdim;
+    a.x = x;
+    a.xrows = t;
+    a.xdiv = top_k;
+    a.y = ws.hbuf;
+    a.ws = ws;
+    hipError_t err = launch_stage_rows<FMT, NB, 2>(a, slots, s);
+    if (err != hipSuccess) return err;
+    MoeStage d{};
+    d.idx = idx;
+    d.p = (int32_t)p;
+    d.e = (int32_t)e;
+    d.inline_group = inl;
+    d.w[0] = wd;
+    d.w[1] = wd;
+    d.n = hdim;
+    d.rb = row_bytes(FMT, f);
+    d.k = (int32_t)f;
+    d.x = ws.hbuf;
+    d.xrows = p;
+    d.xdiv = 1;
+    d.y = ws.dbuf;
+    d.ws = ws;
+    return launch_stage_rows<FMT, NB, 1>(d, slots, s);
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t,
                         int top_k, int32_t* idx, float* probs, float* logits, hipStream_t s) {
-    hipLaunchKernelGGL(router_logits_kernel, dim3((unsigned)((e + 3) / 4)), dim3(256), 0, s, wr, e,
-                       h, x, t, logits);
+    const int64_t groups = (t + 3) / 4;
+    hipLaunchKernelGGL(router_logits_kernel,
+                       dim3((unsigned)((e + 3) / 4), (unsigned)(groups < 64 ? groups : 64)),
+                       dim3(256), 0, s, wr, e, h, x, t, logits);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_softmax_kernel, dim3((unsigned)t), dim3(64), 0, s, logits, e, top_k,
-                       idx, probs);
+    if (e <= 128)
+        hipLaunchKernelGGL((topk_softmax_kernel<2>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
+                           top_k, idx, probs);
+    else if (e <= 256)
+        hipLaunchKernelGGL((topk_softmax_kernel<4>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
+                           top_k, idx, probs);
+    else
+        hipLaunchKernelGGL((topk_softmax_kernel<16>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
+                           top_k, idx, probs);
     return hipGetLastError();
 }
 
@@ -355,17 +748,24 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
                       hipStream_t s) {
     const int64_t p = t * top_k;
     MoeWs m = carve(ws, e, t, top_k, f);
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(256), (size_t)(2 * e) * 4, s, idx, p, e, m);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // Tokens per expert never exceed T; batch them four at a time.
-    if (type == kQ4_K) {
-        if (t <= 1) err = launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, p, top_k, m, s);
-        else err = launch_experts<kQ4_K, 4>(wg, wu, wd, e, h, f, x, p, top_k, m, s);
-    } else {
-        if (t <= 1) err = launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, p, top_k, m, s);
-        else err = launch_experts<kQ8_0, 4>(wg, wu, wd, e, h, f, x, p, top_k, m, s);
+    hipError_t err = hipSuccess;
+    if (p > kInlinePairs) {
+        hipLaunchKernelGGL(group_kernel, dim3(1), dim3(256), (size_t)(2 * e) * 4, s, idx, p, e, m);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
+    // Tokens per expert never exceed T: the token group holds up to 16.
+    const bool q4 = type == kQ4_K;
+    if (t <= 1) err = q4 ? launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
+                         : launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
+    else if (t <= 2) err = q4 ? launch_experts<kQ4_K, 2>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
+                              : launch_experts<kQ8_0, 2>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
+    else if (t <= 4) err = q4 ? launch_experts<kQ4_K, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
+                              : launch_experts<kQ8_0, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
+    else if (t <= 8) err = q4 ? launch_experts<kQ4_K, 8>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
+                              : launch_experts<kQ8_0, 8>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
+    else err = q4 ? launch_experts<kQ4_K, 16>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
+                  : launch_experts<kQ8_0, 16>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((h + 255) / 256), (unsigned)t), dim3(256), 0,
                        s, m.dbuf, idx, probs, e, h, top_k, y);
