@@ -322,7 +322,13 @@ __device__ __forceinline__ bool mnext(const MJobs& jobs, const MPos& p, MPos& q)
         q.chunk = p.chunk + 1;
         return true;
     }
-    const int tn = p.tile + (int)gridDim.x;
+    // Workgroup b takes tile b in round 0, G-1-b in round 1, b in round 2, ...
+    // (G = grid size): with the longest jobs numbered first, the workgroups that
+    // drew a long tile in round 0 are the last to be served in round 1.
+    const int g = (int)gridDim.x;
+    const int r = p.tile / g;
+    const int b = (r & 1) ? g - 1 - p.tile % g : p.tile % g;
+    const int tn = (r + 1) * g + (((r + 1) & 1) ? g - 1 - b : b);
     if (tn >= jobs.total_tiles) return false;
     q = mlocate<RWG>(jobs, tn, 0);
     return true;
@@ -552,6 +558,13 @@ hipError_t launch_main(MJobs& jobs, int batch, hipStream_t s) {
             v = 1;
         per_cu = v;
     }
+    // number the tiles of the longest-K jobs first (stable order otherwise)
+    for (int i = 1; i < jobs.count; ++i)
+        for (int j = i; j > 0 && jobs.j[j].k > jobs.j[j - 1].k; --j) {
+            const MJob t = jobs.j[j];
+            jobs.j[j] = jobs.j[j - 1];
+            jobs.j[j - 1] = t;
+        }
     int total = 0;
     for (int i = 0; i < jobs.count; ++i) {
         MJob& jb = jobs.j[i];
