@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain device copy of known size (HBM counter calibration)")
     p.add_argument("--only", choices=["q4k", "moe", "gemm"], default=None,
                    help="run one secondary workload only (for profiling)")
     return p.parse_args()
@@ -97,6 +99,9 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
+    if args.calibrate_copy:
+        print(json.dumps(calibrate_copy(torch)), flush=True)
+        return
     if args.only:
         print(json.dumps(secondary(g, torch, synth, only=args.only)), flush=True)
         return
@@ -202,7 +207,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom),
             "alg_bytes_per_launch": alg[dom],
             "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches": dom_n,
@@ -215,6 +220,53 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth, shapes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------- #
+COPY_BYTES = 512 << 20
+COPY_REPS = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q8_0_layer_set.json")
+
+
+def calibrate_copy(torch):
+    """A plain device-to-device copy of COPY_BYTES, COPY_REPS times: the HBM
+    counters of its kernel (FETCH_SIZE, WRITE_SIZE) against the known bytes give
+    the counters' scale factors."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "reps": COPY_REPS}
+
+
+def kernel_sources_digest():
+    """sha256 over the native sources; counter-derived traffic is reported only
+    while it matches the sources the counters were taken from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_gguf_q8_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the calibrated counter runs
+    recorded in TRAFFIC_FILE, or None when absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 # --------------------------------------------------------------------------- #
