@@ -108,6 +108,54 @@ __device__ __forceinline__ void decode_unit(const uint8_t* row, int s, float (&f
     }
 }
 
+// One 32-weight half of the unit decode_unit covers (half 0: the first Q8_0
+// block / the low nibbles; half 1: the second block / the high nibbles), for
+// callers that keep fewer registers live.
+template <int FMT>
+__device__ __forceinline__ void decode_half(const uint8_t* row, int s, int half, float (&f)[32],
+                                            float& sa, float& mb) {
+    if constexpr (FMT == kQ8_0) {
+        const uint32_t* u = reinterpret_cast<const uint32_t*>(row + s * 68);
+        if (half == 0) {
+            uint32_t dw[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) dw[i] = u[i];
+            sa = half_bits_to_float(dw[0]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t q = __builtin_amdgcn_alignbyte(dw[i + 1], dw[i], 2);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[4 * i + j] = sbyte_f(q, j);
+            }
+        } else {
+            sa = half_bits_to_float(u[8] >> 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t q = u[9 + i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[4 * i + j] = sbyte_f(q, j);
+            }
+        }
+        mb = 0.f;
+    } else {
+        const uint8_t* sb = row + (s >> 2) * kQ4Bytes;
+        const int g = s & 3;
+        const uint4 hd = *reinterpret_cast<const uint4*>(sb);
+        const Q4KScales sc = q4k_unpack(hd.y, hd.z, hd.w);
+        uint32_t scj, mj;
+        q4k_sub(sc, 2 * g + half, scj, mj);
+        sa = half_bits_to_float(hd.x) * (float)scj;
+        mb = half_bits_to_float(hd.x >> 16) * (float)mj;
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(sb + 16 + 32 * g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t v = half ? (q[i] >> 4) & 0x0F0F0F0Fu : q[i] & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[4 * i + j] = ubyte_f(v, j);
+        }
+    }
+}
+
 // xrow[b]: activation row b (valid for b < batch).  w[m]: base of matrix m.
 // epi(b, r, v): v[m] is the finished product of row r with activation row b.
 template <int FMT, int NB, int ROWS, int NMAT, class Epi>

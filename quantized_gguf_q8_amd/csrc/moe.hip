@@ -489,32 +489,30 @@ __device__ __forceinline__ void moe_compute(const MoeStage& st, const MoeUnit& u
     const int k0 = u.chunk * C::KC;
     const int batch = min(NB, u.cnt - u.g0);
     if (u.r0 + rl < st.n && k0 + s * 64 < st.k) {
+        // one 32-weight half at a time: fewer live registers, more resident waves
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-            float f0[32], f1[32];
-            float sa0, sa1, mb0, mb1;
-            decode_unit<FMT>(lw + (m * ROWS + rl) * C::WRS, s, f0, f1, sa0, sa1, mb0, mb1);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if (b < batch) {
-                    const float4* xv = reinterpret_cast<const float4*>(lx + b * C::XBS + s * C::XSS);
-                    float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int hf = 0; hf < 2; ++hf) {
+                float f[32];
+                float sa, mb;
+                decode_half<FMT>(lw + (m * ROWS + rl) * C::WRS, s, hf, f, sa, mb);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        float4 a = xv[i];
-                        float4 e = xv[8 + i];
-                        p0[i & 3] += f0[4 * i] * a.x + f0[4 * i + 1] * a.y + f0[4 * i + 2] * a.z +
-                                     f0[4 * i + 3] * a.w;
-                        p1[i & 3] += f1[4 * i] * e.x + f1[4 * i + 1] * e.y + f1[4 * i + 2] * e.z +
-                                     f1[4 * i + 3] * e.w;
+                for (int b = 0; b < NB; ++b) {
+                    if (b < batch) {
+                        const float4* xv = reinterpret_cast<const float4*>(
+                            lx + b * C::XBS + s * C::XSS + 32 * hf);
+                        float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const float4 a = xv[i];
+                            p[i & 3] += f[4 * i] * a.x + f[4 * i + 1] * a.y + f[4 * i + 2] * a.z +
+                                        f[4 * i + 3] * a.w;
+                        }
+                        float t = sa * ((p[0] + p[1]) + (p[2] + p[3]));
+                        if constexpr (FMT == kQ4_K) t -= mb * lsum[(b * SL + s) * 2 + hf];
+                        acc[m][b] += t;
                     }
-                    float t = sa0 * ((p0[0] + p0[1]) + (p0[2] + p0[3])) +
-                              sa1 * ((p1[0] + p1[1]) + (p1[2] + p1[3]));
-                    if constexpr (FMT == kQ4_K) {
-                        const float* xs = lsum + (b * SL + s) * 2;
-                        t -= mb0 * xs[0] + mb1 * xs[1];
-                    }
-                    acc[m][b] += t;
                 }
             }
         }
@@ -754,18 +752,17 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    // Tokens per expert never exceed T: the token group holds up to 16.
+    // Tokens per expert never exceed T.  Groups hold up to 4 tokens: with top-k
+    // routing most experts draw one to three tokens of a decode batch, and the
+    // small group keeps LDS and registers low enough for three workgroups per
+    // compute unit; an expert with more tokens is walked once per group.
     const bool q4 = type == kQ4_K;
     if (t <= 1) err = q4 ? launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
                          : launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
     else if (t <= 2) err = q4 ? launch_experts<kQ4_K, 2>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
                               : launch_experts<kQ8_0, 2>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
-    else if (t <= 4) err = q4 ? launch_experts<kQ4_K, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
-                              : launch_experts<kQ8_0, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
-    else if (t <= 8) err = q4 ? launch_experts<kQ4_K, 8>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
-                              : launch_experts<kQ8_0, 8>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
-    else err = q4 ? launch_experts<kQ4_K, 16>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
-                  : launch_experts<kQ8_0, 16>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
+    else err = q4 ? launch_experts<kQ4_K, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
+                  : launch_experts<kQ8_0, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((h + 255) / 256), (unsigned)t), dim3(256), 0,
                        s, m.dbuf, idx, probs, e, h, top_k, y);
