@@ -1,29 +1,21 @@
-// gemv_core.h -- the workgroup-level decode GEMV shared by quant_gemv and the
-// routed-expert kernels.
+// gemv_core.h -- the decode-GEMV building blocks shared by quant_gemv's
+// streaming kernel and the routed-expert kernels.
 //
-// Computes, for ROWS consecutive rows r of NMAT quantized matrices (same shape,
-// same activations) and up to NB activation rows b:
-//     v[m][b][r] = sum_c w_m[r][c] * x_b[c]
-// and hands each finished value to an epilogue functor.  Phobos README,
-// "Inference": the per-token product over GGUF weights; the routed experts reuse
-// it with gathered activations (README opening paragraph).
+// Per-token products over GGUF weights (Phobos README, "Inference"); the routed
+// experts reuse them with gathered activations (README opening paragraph).
 //
-// Decomposition (256 threads, wave64):
-//  * The 256 threads are SL = 256/ROWS K-slices of each row (slice fastest);
-//    a thread's unit is 64 consecutive weights: two Q8_0 blocks (68 bytes) or one
-//    64-weight quarter of a Q4_K super-block (the 16-byte header + 32 quant bytes).
-//  * K is walked in chunks of KC = 64*SL weights.  A chunk of a row is contiguous
-//    in memory; the workgroup copies the chunk of all its rows to LDS with 16-byte
-//    loads, coalesced along each row, so the 34-byte Q8_0 blocks never need
-//    unaligned global loads.  The activation chunk is staged beside it, padded per
-//    slice so the 16 slices a wave reads land in distinct LDS bank groups.
-//  * A thread decodes its unit once into registers and applies it to every
-//    activation row: one read of the weights serves the whole batch.
-//  * The SL partials of a row are summed through LDS in a fixed order, so the
-//    result does not depend on timing.
-//  * Q4_K is evaluated per 32-weight sub-block j in the factored form
-//        d*sc_j * sum q_c x_c  -  dmin*m_j * sum x_c,
-//    with sum x_c computed once per chunk while the activations are staged.
+// Thread layout: a workgroup of 256 threads covers ROWS rows, each row split
+// into SL = 256/ROWS K-slices (slice fastest, so a row's slices are lanes of one
+// wave).  A thread's unit is 64 consecutive weights of its row -- two Q8_0
+// blocks (68 bytes) or a 64-weight quarter of a Q4_K super-block (its 16-byte
+// header + 32 quant bytes) -- and K is walked in chunks of KC = 64*SL weights.
+// A chunk of a row is contiguous in memory, so the row chunks of a tile are
+// copied to LDS with coalesced 16-byte loads (34-byte Q8_0 blocks never need
+// unaligned global loads); the activation chunk is staged beside it, padded per
+// slice so the slices a wave reads land in distinct LDS bank groups.
+// Q4_K is evaluated per 32-weight sub-block j in the factored form
+//     d*sc_j * sum q_c x_c  -  dmin*m_j * sum x_c,
+// with sum x_c formed once per chunk while the activations are staged.
 #pragma once
 
 #include "ggq_device.h"
@@ -46,9 +38,6 @@ struct GemvCfg {
     static constexpr int kWBytes = NMAT * ROWS * WRS;
     static constexpr int kXBytes = NB * XBS * 4;
     static constexpr int kSumBytes = FMT == kQ4_K ? NB * SL * 2 * 4 : 0;
-    static constexpr int kRedBytes = NMAT * NB * ROWS * (SL + 1) * 4;
-    static constexpr int kMain = kWBytes + kXBytes + kSumBytes;
-    static constexpr int kLds = kMain > kRedBytes ? kMain : kRedBytes;
     static_assert(SL % 4 == 0 && SL <= 64, "slice count");
     static_assert(CRB % 16 == 0, "chunk rows must be whole 16-byte pieces");
     static_assert((NB * KC / 4) % 64 == 0, "activation staging must use whole waves");
@@ -152,129 +141,6 @@ __device__ __forceinline__ void decode_half(const uint8_t* row, int s, int half,
             const uint32_t v = half ? (q[i] >> 4) & 0x0F0F0F0Fu : q[i] & 0x0F0F0F0Fu;
 #pragma unroll
             for (int j = 0; j < 4; ++j) f[4 * i + j] = ubyte_f(v, j);
-        }
-    }
-}
-
-// xrow[b]: activation row b (valid for b < batch).  w[m]: base of matrix m.
-// epi(b, r, v): v[m] is the finished product of row r with activation row b.
-template <int FMT, int NB, int ROWS, int NMAT, class Epi>
-__device__ __forceinline__ void gemv_tile(uint8_t* lds, const uint8_t* const (&w)[NMAT], int64_t n,
-                                          int k, int64_t rbytes, const float* const (&xrow)[NB],
-                                          int batch, int64_t r0, Epi& epi) {
-    using C = GemvCfg<FMT, NB, ROWS, NMAT>;
-    constexpr int SL = C::SL;
-    constexpr int KC = C::KC;
-    uint8_t* lw = lds;
-    float* lx = reinterpret_cast<float*>(lds + C::kWBytes);
-    float* lsum = reinterpret_cast<float*>(lds + C::kWBytes + C::kXBytes);
-
-    const int tid = threadIdx.x;
-    const int s = tid % SL;
-    const int rl = tid / SL;
-    const bool row_ok = r0 + rl < n;
-
-    float acc[NMAT][NB];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[m][b] = 0.f;
-
-    const int nchunks = (k + KC - 1) / KC;
-    for (int c = 0; c < nchunks; ++c) {
-        const int k0 = c * KC;
-        {   // weights: NMAT x ROWS rows x CRB bytes as 16-byte pieces
-            constexpr int PPR = C::CRB / 16;
-            const int64_t cb0 = (int64_t)c * C::CRB;
-            for (int p = tid; p < NMAT * ROWS * PPR; p += 256) {
-                int m = p / (ROWS * PPR);
-                int pr = (p / PPR) % ROWS;
-                int off = (p % PPR) * 16;
-                if (r0 + pr < n && cb0 + off < rbytes) {
-                    const uint4* src =
-                        reinterpret_cast<const uint4*>(w[m] + (r0 + pr) * rbytes + cb0 + off);
-                    *reinterpret_cast<uint4*>(lw + (m * ROWS + pr) * C::WRS + off) = *src;
-                }
-            }
-        }
-        {   // activations [NB][KC] (+ per-32 sums for Q4_K)
-            constexpr int P4 = KC / 4;
-            for (int p = tid; p < NB * P4; p += 256) {
-                int b = p / P4;
-                int pos = (p % P4) * 4;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (b < batch && k0 + pos < k)
-                    v = *reinterpret_cast<const float4*>(xrow[b] + k0 + pos);
-                *reinterpret_cast<float4*>(lx + b * C::XBS + (pos >> 6) * C::XSS + (pos & 63)) = v;
-                if constexpr (FMT == kQ4_K) {
-                    // 8 consecutive lanes hold one 32-weight run
-                    float t = (v.x + v.y) + (v.z + v.w);
-                    t += __shfl_xor(t, 1, 64);
-                    t += __shfl_xor(t, 2, 64);
-                    t += __shfl_xor(t, 4, 64);
-                    if ((p & 7) == 0) lsum[(b * SL + (pos >> 6)) * 2 + ((pos >> 5) & 1)] = t;
-                }
-            }
-        }
-        __syncthreads();
-
-        if (row_ok && k0 + s * 64 < k) {
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                float f0[32], f1[32];
-                float sa0, sa1, mb0, mb1;
-                decode_unit<FMT>(lw + (m * ROWS + rl) * C::WRS, s, f0, f1, sa0, sa1, mb0, mb1);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (b < batch) {
-                        const float4* xv =
-                            reinterpret_cast<const float4*>(lx + b * C::XBS + s * C::XSS);
-                        float p0[4] = {0.f, 0.f, 0.f, 0.f}, p1[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            float4 a = xv[i];
-                            float4 e = xv[8 + i];
-                            p0[i & 3] += f0[4 * i] * a.x + f0[4 * i + 1] * a.y +
-                                         f0[4 * i + 2] * a.z + f0[4 * i + 3] * a.w;
-                            p1[i & 3] += f1[4 * i] * e.x + f1[4 * i + 1] * e.y +
-                                         f1[4 * i + 2] * e.z + f1[4 * i + 3] * e.w;
-                        }
-                        float s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]);
-                        float s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
-                        float t = sa0 * s0 + sa1 * s1;
-                        if constexpr (FMT == kQ4_K) {
-                            const float* xs = lsum + (b * SL + s) * 2;
-                            t -= mb0 * xs[0] + mb1 * xs[1];
-                        }
-                        acc[m][b] += t;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // slice partials -> LDS -> fixed-order sums
-    float* red = reinterpret_cast<float*>(lds);
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) red[((m * NB + b) * ROWS + rl) * (SL + 1) + s] = acc[m][b];
-    __syncthreads();
-    for (int o = tid; o < NB * ROWS; o += 256) {
-        int b = o / ROWS;
-        int r = o % ROWS;
-        if (b < batch && r0 + r < n) {
-            float v[NMAT];
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                const float* q = red + ((m * NB + b) * ROWS + r) * (SL + 1);
-                float pr[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < SL; ++i) pr[i & 3] += q[i];
-                v[m] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-            }
-            epi(b, r0 + r, v);
         }
     }
 }
