@@ -202,7 +202,9 @@ struct GemmShape {
     static constexpr int UNITS = BN * (kBK / 16);            // decode units per step
     static constexpr int UPW = (UNITS + WV - 1) / WV;       // per wave
     static constexpr int UPT = (UPW + 63) / 64;             // per thread
-    static constexpr int kBuf = BN * kLRow;                 // bf16 elements per buffer
+    // bf16 elements per buffer: BN rows plus one row that absorbs the stores of
+    // lanes without a decode unit (so the decode has no branch)
+    static constexpr int kBuf = (BN + 1) * kLRow;
     static constexpr int kLds = 2 * kBuf * 2;               // bytes
 };
 
@@ -301,8 +303,8 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
         for (int i = 0; i < S::UPT; ++i) {
             const int qi = lane + 64 * i;
             const int q = S::UPW * wave + qi;
-            if (qi < S::UPW && q < S::UNITS)
-                store_unit<FMT>(src[i], q % 4, step * kBK, buf + (q / 4) * kLRow);
+            const int row = (qi < S::UPW && q < S::UNITS) ? q / 4 : S::BN;
+            store_unit<FMT>(src[i], q % 4, step * kBK, buf + row * kLRow);
         }
     };
 
@@ -319,10 +321,13 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
             const int ks = ks0 + d;
             bf16x8 (&acur)[2][4] = (d & 1) ? an : af;
             bf16x8 (&anext)[2][4] = (d & 1) ? af : an;
-            // ring slot d held step ks (decoded during the previous step): refill
-            // it with step ks + kDW, and fetch the next step's A fragments
-            load_w(ks + kDW, ru[d]);
+            // fetch the next step's A fragments, then refill ring slot d (it held
+            // step ks, decoded during the previous step) with step ks + kDW.  The
+            // order matters: loads complete in issue order as far as the wait
+            // counter is concerned, so A issued before the weights lets the next
+            // step's MFMAs wait only for weights fetched steps earlier.
             load_a(ks + 1, anext);
+            load_w(ks + kDW, ru[d]);
             const uint16_t* bbase =
                 wl + (d & 1) * S::kBuf + (lane & 15) * kLRow + 8 * (lane >> 4);
 #pragma unroll
