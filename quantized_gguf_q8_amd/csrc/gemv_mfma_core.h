@@ -52,7 +52,7 @@ __host__ __device__ inline XfLayout xf_layout(int type, int64_t k, int mt) {
     L.mins = al256((int64_t)mt * (k / 32) * 1024);
     const int64_t mb = type == kQ4_K ? (int64_t)mt * (k / 256) * 512 : 0;
     L.inv = L.mins + al256(mb);
-    L.bytes = L.inv + 256;
+    L.bytes = L.inv + al256((int64_t)mt * 8 * 4);   // 2^-S per padded row
     return L;
 }
 

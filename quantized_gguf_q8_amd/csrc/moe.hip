@@ -20,12 +20,12 @@
 //                writes the lists to the workspace first.
 //   2. gate/up : per (selected expert, row tile): the same rows of that expert's
 //                gate and up matrices against every token routed to it,
-//                epilogue h = silu(g) * u.
+//                epilogue h = silu(g) * u (matrix cores from two tokens on).
 //   3. down    : per (selected expert, row tile): d = Wd h for each of its pairs.
 //   4. combine : y[t] = sum_s probs[t][s] * d_(t,s) in slot order.
 // Only the selected experts' bytes are read, once per group of up to 16 tokens
 // routed to the expert, and nothing is accumulated with atomics.
-#include "gemv_core.h"
+#include "gemv_mfma_core.h"
 #include "ggq_launch.h"
 
 namespace ggq {
@@ -153,13 +153,17 @@ struct MoeWs {
     int32_t* list;    // [P]   pair ids (t*top_k + s) sorted by (expert, pair)
     float* hbuf;      // [P][F]
     float* dbuf;      // [P][H]
+    uint8_t* xfx;     // matrix-core path: fragments of x (xf_layout(Q4_K, H, T/8))
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 inline size_t ints_bytes(int64_t e, int64_t p) { return align256((size_t)(3 * e + 1 + p) * 4); }
 
-MoeWs carve(void* ws, int64_t e, int64_t t, int top_k, int64_t f) {
+// Fragment regions are sized with the Q4_K layout, which is the larger one.
+inline size_t xfx_bytes(int64_t t, int64_t h) { return (size_t)xf_layout(kQ4_K, h, (int)((t + 7) / 8)).bytes; }
+
+MoeWs carve(void* ws, int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
     const int64_t p = t * top_k;
     uint8_t* base = static_cast<uint8_t*>(ws);
     MoeWs m;
@@ -171,6 +175,7 @@ MoeWs carve(void* ws, int64_t e, int64_t t, int top_k, int64_t f) {
     m.list = iw + 3 * e + 1;
     m.hbuf = reinterpret_cast<float*>(base + ints_bytes(e, p));
     m.dbuf = reinterpret_cast<float*>(base + ints_bytes(e, p) + align256((size_t)p * f * 4));
+    m.xfx = reinterpret_cast<uint8_t*>(m.dbuf) + align256((size_t)p * h * 4);
     return m;
 }
 
@@ -596,6 +601,215 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
     }
 }
 
+// ------------------------------------------------- matrix-core stage ----
+// For two or more tokens the gate/up stage runs on the matrix cores, like the
+// batched decode GEMV (with 1-3 tokens per expert the fp32 decode-and-FMA path
+// is bound by the vector units there): the tokens are split once per call into
+// exact fp16 hi/lo fragments by xfrag_kernel; a unit is one K chunk of 64
+// B-operand rows of one selected expert (NMAT = 2: 32 rows of each matrix,
+// waves 0-1 gate and 2-3 up; NMAT = 1: 64 rows of one matrix) for one group of
+// up to 8 of its tokens, whose fragment rows are gathered lane by lane from the
+// per-call fragments.  Weights are staged with 16-byte loads one unit ahead, as
+// in the other streaming kernels.
+struct MoeMfma {
+    const uint8_t* w[2];   // expert-stacked matrices [E][n][rb]
+    int64_t n, rb;         // rows per expert matrix, bytes per row
+    int32_t k, nchunk, tiles;
+    const uint8_t* xf;     // fragments of the activation rows
+    int32_t xmt;           // 8-row tiles in xf
+    int32_t xdiv;          // activation row of pair p: p / xdiv
+    float* y;              // output row of pair p: y + p * n
+    MoeWs ws;
+    const int32_t* idx;
+    int32_t p, e, inline_group;
+};
+
+template <int FMT, int NMAT>
+struct MoeMCfg {
+    using C = MCfg<FMT, 1, 4>;         // 64 B rows, chunk KC, fragments of 8 slots
+    static constexpr int RPM = 64 / NMAT;                 // rows of each matrix per tile
+    static constexpr int PPR = C::CRB / 16;                // 16-byte pieces per row chunk
+    static constexpr int WPIECES = 64 * PPR;
+    static constexpr int WP = (WPIECES + 255) / 256;
+    static constexpr int FPIECES = C::kFrag / 16;          // 16-byte fragment pieces
+    static constexpr int FP = (FPIECES + 255) / 256;
+    static constexpr int MPIECES = C::kMins / 8;           // 8-byte min-term pieces
+    static constexpr int MP = (MPIECES + 255) / 256;
+    static constexpr int kInvOff = C::kW + C::kFrag + C::kMins;
+    static constexpr int kBuf = kInvOff + 32;              // + 2^-S of the 8 slots
+    static constexpr int kRed = NMAT == 2 ? 2 * 64 * 2 * 4 : 0;
+    static constexpr int kLds = 2 * kBuf + kRed;
+};
+
+template <int FMT, int NMAT>
+struct MoeMPrefetch {
+    using M = MoeMCfg<FMT, NMAT>;
+    using C = typename M::C;
+    uint4 w[M::WP];
+    uint4 f[M::FP];
+    uint2 mn[M::MP > 0 ? M::MP : 1];
+    float inv;
+
+    __device__ __forceinline__ void load(const MoeMfma& st, const MoeUnit& u, int tid) {
+        const int batch = min(8, u.cnt - u.g0);
+        const uint32_t cb0 = (uint32_t)u.chunk * C::CRB;
+        // weights: B row br = m * RPM + rr; per-lane addresses (the matrix varies
+        // within a wave), clamped to a valid byte and zeroed when out of range
+#pragma unroll
+        for (int i = 0; i < M::WP; ++i) {
+            const int q = tid + 256 * i;
+            const int br = q / M::PPR, off = (q % M::PPR) * 16;
+            const int m = br / M::RPM;
+            const int64_t r = u.r0 + br % M::RPM;
+            const bool ok = q < M::WPIECES && r < st.n && cb0 + off < st.rb;
+            const uint8_t* src = st.w[m < NMAT ? m : 0] + ((int64_t)u.e * st.n + (ok ? r : 0)) * st.rb +
+                                 (ok ? cb0 + off : 0);
+            const uint4 v = load_once16(src);
+            w[i] = ok ? v : make_uint4(0, 0, 0, 0);
+        }
+        // activation fragments gathered per slot: lane l of block b holds slot
+        // (l % 16) / 2, hi/lo l % 2, k-octet l / 16
+        const XfLayout L = xf_layout(FMT, st.k, st.xmt);
+        const __amdgpu_buffer_rsrc_t rf = make_rsrc(st.xf, (uint32_t)L.bytes);
+        const int nblk = st.k / 32, nsb = st.k / 256;
+#pragma unroll
+        for (int i = 0; i < M::FP; ++i) {
+            const int q = tid + 256 * i;
+            const int blk = q / 64, l = q % 64;
+            const int sl = (l & 15) >> 1;
+            uint32_t off = kOob;
+            const int kb = u.chunk * C::NBLK + blk;
+            if (q < M::FPIECES && sl < batch && kb < nblk) {
+                const int row = u.xrows ? u.xrows[u.g0 + sl] : u.pairs[u.g0 + sl] / st.xdiv;
+                const int sln = 2 * (row & 7) + (l & 1) + 16 * (l >> 4);
+                off = (uint32_t)(L.frag + (((int64_t)(row >> 3) * nblk + kb) * 64 + sln) * 16);
+            }
+            f[i] = buf_load16<false>(rf, off);
+        }
+        if constexpr (FMT == kQ4_K) {
+#pragma unroll
+            for (int i = 0; i < M::MP; ++i) {
+                const int q = tid + 256 * i;
+                const int sb = q / 64, l = q % 64;
+                const int sl = (l & 15) >> 1;
+                const int ksb = u.chunk * C::NSB + sb;
+                uint32_t off = kOob;
+                if (q < M::MPIECES && sl < batch && (l >> 4) < 2 && ksb < nsb) {
+                    const int row = u.xrows ? u.xrows[u.g0 + sl] : u.pairs[u.g0 + sl] / st.xdiv;
+                    const int sln = 2 * (row & 7) + (l & 1) + 16 * (l >> 4);
+                    off = (uint32_t)(L.mins + (((int64_t)(row >> 3) * nsb + ksb) * 64 + sln) * 8);
+                }
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rf, off, 0, 0);
+                mn[i] = make_uint2(v.x, v.y);
+            }
+        }
+        inv = 1.f;
+        if (tid < batch) {
+            const int row = u.xrows ? u.xrows[u.g0 + tid] : u.pairs[u.g0 + tid] / st.xdiv;
+            inv = reinterpret_cast<const float*>(st.xf + L.inv)[row];
+        }
+    }
+
+    __device__ __forceinline__ void store(uint8_t* buf, int tid) const {
+#pragma unroll
+        for (int i = 0; i < M::WP; ++i) {
+            const int q = tid + 256 * i;
+            if (q < M::WPIECES)
+                *reinterpret_cast<uint4*>(buf + (q / M::PPR) * C::RS + (q % M::PPR) * 16) = w[i];
+        }
+#pragma unroll
+        for (int i = 0; i < M::FP; ++i) {
+            const int q = tid + 256 * i;
+            if (q < M::FPIECES) *reinterpret_cast<uint4*>(buf + C::kW + q * 16) = f[i];
+        }
+        if constexpr (FMT == kQ4_K) {
+#pragma unroll
+            for (int i = 0; i < M::MP; ++i) {
+                const int q = tid + 256 * i;
+                if (q < M::MPIECES) *reinterpret_cast<uint2*>(buf + C::kW + C::kFrag + q * 8) = mn[i];
+            }
+        }
+        if (tid < 8) reinterpret_cast<float*>(buf + M::kInvOff)[tid] = inv;
+    }
+};
+
+template <int FMT, int NMAT>
+__global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
+    using M = MoeMCfg<FMT, NMAT>;
+    using C = typename M::C;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;   // B column = row 16 * wave + j of the tile
+    const int h = lane >> 4;   // D rows 4h .. 4h+3 = slots 2h, 2h+1 (hi, lo)
+
+    MoeLists L;
+    if (st.inline_group) {
+        L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lds + M::kLds));
+    } else {
+        L = MoeLists{st.ws.cnt, st.ws.off, st.ws.active, st.ws.list, nullptr, st.ws.nact[0]};
+    }
+    const int total = L.nact * st.tiles;
+
+    MoeStage ms{};   // unit walk shared with the streaming kernels
+    ms.nchunk = st.nchunk;
+    ms.tiles = st.tiles;
+    MoeUnit cur;
+    if (!moe_locate<M::RPM>(ms, L, blockIdx.x, total, cur)) return;
+    MoeMPrefetch<FMT, NMAT> pf;
+    pf.load(st, cur, tid);
+    pf.store(lds, tid);
+    __syncthreads();
+
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    int buf = 0;
+    for (;;) {
+        MoeUnit nxt;
+        const bool more = moe_next<8, M::RPM>(ms, L, cur, total, nxt);
+        if (more) pf.load(st, nxt, tid);
+        const uint8_t* base = lds + buf * M::kBuf;
+        mfma_chunk<FMT, 1, 4>(base, cur.chunk * C::KC, st.k, lane, wave, 0, j, h, acc);
+        if (cur.chunk == st.nchunk - 1) {
+            const float* invb = reinterpret_cast<const float*>(base + M::kInvOff);
+            const int batch = min(8, cur.cnt - cur.g0);
+            const int br = 16 * wave + j;
+            const int64_t r = cur.r0 + br % M::RPM;
+            const float v0 = (acc[0][0] + acc[0][1]) * invb[2 * h];
+            const float v1 = (acc[0][2] + acc[0][3]) * invb[2 * h + 1];
+            if constexpr (NMAT == 2) {
+                // up rows (waves 2, 3) hand their values to the gate rows (waves 0, 1)
+                float* red = reinterpret_cast<float*>(lds + 2 * M::kBuf);
+                if (wave >= 2) {
+                    red[((wave - 2) * 64 + lane) * 2] = v0;
+                    red[((wave - 2) * 64 + lane) * 2 + 1] = v1;
+                }
+                __syncthreads();
+                if (wave < 2 && r < st.n) {
+                    const float u0 = red[(wave * 64 + lane) * 2], u1 = red[(wave * 64 + lane) * 2 + 1];
+                    if (2 * h < batch)
+                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.n + r] = v0 / (1.0f + expf(-v0)) * u0;
+                    if (2 * h + 1 < batch)
+                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.n + r] = v1 / (1.0f + expf(-v1)) * u1;
+                }
+                __syncthreads();
+            } else {
+                if (r < st.n) {
+                    if (2 * h < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.n + r] = v0;
+                    if (2 * h + 1 < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.n + r] = v1;
+                }
+            }
+            acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (!more) break;
+        buf ^= 1;
+        pf.store(lds + buf * M::kBuf, tid);
+        __syncthreads();
+        cur = nxt;
+    }
+}
+
 // y[t][r] = sum_s probs[t][s] * d[(t*top_k + s)][r], slot order; pairs whose
 // expert index is out of range contribute nothing.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ dbuf,
@@ -669,6 +883,93 @@ hipError_t launch_stage_rows(const MoeStage& st, int64_t slots, hipStream_t s) {
     return launch_stage<FMT, NB, 32, NMAT>(st, slots, s);
 }
 
+template <int FMT, int NMAT>
+hipError_t launch_mstage(MoeMfma st, int64_t slots, hipStream_t s) {
+    using M = MoeMCfg<FMT, NMAT>;
+    using C = typename M::C;
+    const size_t lds = M::kLds + (st.inline_group ? inline_group_bytes(st.e, st.p) : 0);
+    static size_t per_cu_lds = 0;
+    static int per_cu = 0;
+    if (per_cu_lds != lds) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_mfma_kernel<FMT, NMAT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_mfma_kernel<FMT, NMAT>, 256, lds) !=
+                hipSuccess || v <= 0)
+            v = 1;
+        per_cu = v;
+        per_cu_lds = lds;
+    }
+    st.nchunk = (st.k + C::KC - 1) / C::KC;
+    st.tiles = (int32_t)((st.n + M::RPM - 1) / M::RPM);
+    const int64_t most = slots * st.tiles;
+    const int64_t cap = (int64_t)per_cu * moe_device_cus();
+    const unsigned grid = (unsigned)(most < cap ? most : cap);
+    hipLaunchKernelGGL((moe_mfma_kernel<FMT, NMAT>), dim3(grid), dim3(256), lds, s, st);
+    return hipGetLastError();
+}
+
+// Split `rows` activation rows of K floats into the fragments at xf.
+template <int FMT>
+hipError_t launch_split(const float* x, int64_t rows, int64_t k, uint8_t* xf, hipStream_t s) {
+    MJobs jobs{};
+    jobs.count = 1;
+    jobs.j[0].x = x;
+    jobs.j[0].xf = xf;
+    jobs.j[0].ldx = k;
+    jobs.j[0].k = (int32_t)k;
+    const int mt = (int)((rows + 7) / 8);
+    const dim3 grid((unsigned)(mt * 8), (unsigned)((k / 32 + kXfragSlice - 1) / kXfragSlice));
+    hipLaunchKernelGGL(xfrag_kernel<FMT>, grid, dim3(256), 0, s, jobs, (int)rows, mt);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
+                               int64_t e, int64_t hdim, int64_t f, const float* x, int64_t t,
+                               int top_k, const int32_t* idx, const MoeWs& ws, hipStream_t s) {
+    const int64_t p = t * top_k;
+    const int64_t slots = p < e ? p : e;
+    const bool inl = p <= kInlinePairs;
+    hipError_t err = launch_split<FMT>(x, t, hdim, ws.xfx, s);
+    if (err != hipSuccess) return err;
+    MoeMfma a{};
+    a.w[0] = wg;
+    a.w[1] = wu;
+    a.n = f;
+    a.rb = row_bytes(FMT, hdim);
+    a.k = (int32_t)hdim;
+    a.xf = ws.xfx;
+    a.xmt = (int32_t)((t + 7) / 8);
+    a.xdiv = top_k;
+    a.y = ws.hbuf;
+    a.ws = ws;
+    a.idx = idx;
+    a.p = (int32_t)p;
+    a.e = (int32_t)e;
+    a.inline_group = inl;
+    err = launch_mstage<FMT, 2>(a, slots, s);
+    if (err != hipSuccess) return err;
+    // The down stage stays on the vector units: with K = F short, splitting h
+    // into fragments costs a launch that the matrix cores do not win back.
+    MoeStage d{};
+    d.idx = idx;
+    d.p = (int32_t)p;
+    d.e = (int32_t)e;
+    d.inline_group = inl;
+    d.w[0] = wd;
+    d.w[1] = wd;
+    d.n = hdim;
+    d.rb = row_bytes(FMT, f);
+    d.k = (int32_t)f;
+    d.x = ws.hbuf;
+    d.xrows = p;
+    d.xdiv = 1;
+    d.y = ws.dbuf;
+    d.ws = ws;
+    return launch_stage_rows<FMT, 4, 1>(d, slots, s);
+}
+
 template <int FMT, int NB>
 hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, int64_t e,
                           int64_t hdim, int64_t f, const float* x, int64_t t, int top_k,
@@ -737,7 +1038,8 @@ size_t moe_ws_h_offset(int64_t e, int64_t t, int top_k) { return ints_bytes(e, t
 
 size_t moe_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
     const int64_t p = t * top_k;
-    return ints_bytes(e, p) + align256((size_t)p * f * 4) + align256((size_t)p * h * 4);
+    return ints_bytes(e, p) + align256((size_t)p * f * 4) + align256((size_t)p * h * 4) +
+           align256(xfx_bytes(t, h));
 }
 
 hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
@@ -745,24 +1047,20 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
                       const int32_t* idx, const float* probs, int top_k, float* y, void* ws,
                       hipStream_t s) {
     const int64_t p = t * top_k;
-    MoeWs m = carve(ws, e, t, top_k, f);
+    MoeWs m = carve(ws, e, t, top_k, h, f);
     hipError_t err = hipSuccess;
     if (p > kInlinePairs) {
         hipLaunchKernelGGL(group_kernel, dim3(1), dim3(256), (size_t)(2 * e) * 4, s, idx, p, e, m);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    // Tokens per expert never exceed T.  Groups hold up to 4 tokens: with top-k
-    // routing most experts draw one to three tokens of a decode batch, and the
-    // small group keeps LDS and registers low enough for three workgroups per
-    // compute unit; an expert with more tokens is walked once per group.
+    // One token: the vector-unit streaming stages.  Two or more: the matrix-core
+    // stages (groups of up to 8 of an expert's tokens per pass).
     const bool q4 = type == kQ4_K;
     if (t <= 1) err = q4 ? launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
                          : launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
-    else if (t <= 2) err = q4 ? launch_experts<kQ4_K, 2>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
-                              : launch_experts<kQ8_0, 2>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
-    else err = q4 ? launch_experts<kQ4_K, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
-                  : launch_experts<kQ8_0, 4>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
+    else err = q4 ? launch_experts_mfma<kQ4_K>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
+                  : launch_experts_mfma<kQ8_0>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((h + 255) / 256), (unsigned)t), dim3(256), 0,
                        s, m.dbuf, idx, probs, e, h, top_k, y);
