@@ -217,6 +217,26 @@ def test_gemv_grouped_parity(g, fmt, specs, b, path):
         check_rel(y, yr, s, GEMV_TOL, f"grouped {n}x{k}")
 
 
+@pytest.mark.parametrize("b,ws", [(1, None), (8, "auto")])
+def test_gemv_layer_set_as_benchmarked(g, b, ws):
+    """The exact launches bench.py times: one grouped call over the whole ~1B
+    Q8_0 layer set (head included) on the benchmark's seeded inputs, batch 1 on
+    the vector units and batch 8 on the matrix cores; every output checked."""
+    say(f"gemv bench launch b={b} ws={ws}")
+    mats, items = [], []
+    for name, n, k in synth.DENSE_1B_LAYER_SET:
+        tid = synth.tid(1, n, k)
+        w = synth.q8_0_matrix(n, k, seed=0, tensor_id=tid)
+        x = synth.normal_f32((b, k), seed=0, tensor_id=tid + b)
+        mats.append((name, w, n, k, x))
+        items.append((dev(w), n, k, dev(x), torch.empty((b, n), device="cuda")))
+    g.GemvGroup(Q8, items, ws=ws)()
+    for (name, w, n, k, x), it in zip(mats, items):
+        yr, s = oracle.gemv(Q8, w, n, k, x)
+        worst = check_rel(host(it[4]), yr, s, GEMV_TOL, f"{name} b{b}")
+        say(f"  {name}: worst err / bound = {worst:.3g}")
+
+
 def test_graph_replays_match_eager(g):
     """Grouped GEMV, GEMM and the MoE layer captured in one HIP graph: every
     replay, with eager work in between, equals the eager result bit for bit."""
