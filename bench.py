@@ -8,8 +8,9 @@ size is one grouped launch over the six matrices (README "Components": kernel
 fusion).  Weights and activations are seeded synthetic tensors with the model's
 shapes, resident in HBM before the timed region.  The weights are cycled over
 enough distinct device copies (>= 1 GiB) that no step finds them in the 256 MB
-last-level cache.  Steps are replayed from HIP graphs (one per weight copy) so the
-host's launch cost is not what is measured.
+last-level cache.  Steps are replayed from HIP graphs -- one graph runs a step
+on each weight copy in turn -- so the host's launch cost is not what is
+measured.
 
 Prints one JSON line: weight GB/s of the step (value), the dominant kernel's
 achieved bandwidth against the 8 TB/s HBM peak (roofline; per-launch HIP events on
@@ -133,16 +134,29 @@ def main():
         g1, g8 = groups[c]
         return lambda: (g1(), g8())
 
-    graphs = capture(torch, [step_fn(c) for c in range(copies)])
-    for i in range(args.warmup):
-        graphs[i % copies].replay()
+    # One graph runs a step on every weight copy in turn (`copies` steps per
+    # replay, as a serving loop captures many layers per graph); single-step
+    # graphs make up a step count that is not a multiple of `copies`.
+    def all_copies():
+        for c in range(copies):
+            step_fn(c)()
+
+    graphs = capture(torch, [step_fn(c) for c in range(copies)] + [all_copies])
+    single, multi = graphs[:copies], graphs[copies]
+
+    def run_steps(n):
+        for _ in range(n // copies):
+            multi.replay()
+        for i in range(n % copies):
+            single[i].replay()
+
+    run_steps(args.warmup)
     torch.cuda.synchronize()
 
-    # ---- timed region: graph replays of K steps ----
+    # ---- timed region: exactly K steps ----
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % copies].replay()
+    run_steps(args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -321,8 +335,9 @@ def secondary(g, torch, synth, only=None):
                     g.moe_expert_gemv(g.Q4_K, wg_, wu_, wd_, e, h, f, x, ii, pp, y, ws)
                 return run
 
-            graphs = capture(torch, [layer(c) for c in range(copies)])
-            ms = replay_ms(torch, graphs, 50 * copies)
+            # one graph runs the layer once on every weight copy
+            graphs = capture(torch, [lambda: [layer(c)() for c in range(copies)]])
+            ms = replay_ms(torch, graphs, 50, copies)
             gbs = alg / (ms * 1e-3) / 1e9
             res[f"t{t}"] = {"us": round(ms * 1e3, 3), "distinct_experts": distinct,
                             "alg_bytes": alg, "GB/s": round(gbs, 1),
@@ -339,8 +354,10 @@ def secondary(g, torch, synth, only=None):
             c = torch.empty((m, n), dtype=torch.float32, device=dev)
             ws = torch.empty(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
                              device=dev)
-            graphs = capture(torch, [lambda: g.quant_gemm(fmt, w, n, k, a, c, ws)])
-            ms = replay_ms(torch, graphs, 30)
+            per = 4   # calls per graph
+            graphs = capture(torch, [lambda: [g.quant_gemm(fmt, w, n, k, a, c, ws)
+                                              for _ in range(per)]])
+            ms = replay_ms(torch, graphs, 10, per)
             tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
             res[name] = {"shape": f"{m}x{n}x{k}", "us": round(ms * 1e3, 2),
                          "TFLOP/s": round(tflops, 1),
