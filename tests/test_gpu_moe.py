@@ -159,6 +159,9 @@ def _small(seed, fmt, e, h, f, t):
 @pytest.mark.parametrize("fmt,e,h,f,t,k", [
     (Q4, 6, 512, 256, 5, 3), (Q8, 9, 768, 512, 7, 4), (Q4, 4, 256, 768, 33, 4),
     (Q8, 130, 256, 256, 3, 32),
+    (Q8, 20, 512, 256, 1, 6),        # one token, Q8_0: the vector-unit stages
+    (Q4, 16, 256, 256, 40, 8),       # 320 pairs: lists built by the grouping kernel
+    (Q8, 12, 512, 256, 70, 4),       # 280 pairs, Q8_0, experts with > 8 tokens
 ])
 def test_moe_small_shapes(g, fmt, e, h, f, t, k):
     say(f"moe small fmt={fmt} e={e} h={h} f={f} t={t} k={k}")
