@@ -257,7 +257,7 @@ def calibrate_copy(torch):
 
 
 def kernel_sources_digest():
-    """sha256 over the native sources; counter-derived traffic is reported only
+    """sha256 over the native sources and build flags; counter-derived traffic is reported only
     while it matches the sources the counters were taken from."""
     import hashlib
     h = hashlib.sha256()
@@ -266,6 +266,8 @@ def kernel_sources_digest():
         if name.endswith((".hip", ".h")):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "quantized_gguf_q8_amd", "build.py"), "rb") as f:
+        h.update(b"build.py\0" + f.read())   # compiler flags change the code too
     return h.hexdigest()
 
 

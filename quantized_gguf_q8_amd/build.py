@@ -37,14 +37,24 @@ def _run(cmd):
     return err
 
 
+# Per-source flags.  The decode GEMV and expert kernels keep MFMA results in
+# ordinary VGPRs: their few accumulators are rescaled by the vector units after
+# every block, and with AGPR results each rescale first needed a v_accvgpr_read.
+FILE_FLAGS = {
+    "gemv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(OBJ, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     with ThreadPoolExecutor(max(1, jobs)) as ex:
-        outs = list(ex.map(lambda so: _run([HIPCC, *CFLAGS, "-c", so[0], "-o", so[1]]),
-                           zip(srcs, objs)))
+        outs = list(ex.map(
+            lambda so: _run([HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(so[0]), []),
+                             "-c", so[0], "-o", so[1]]),
+            zip(srcs, objs)))
     if verbose:
         for o in outs:
             if o.strip():

@@ -6,9 +6,22 @@
 // Work decomposition: a workgroup (4 waves) owns 16*WM rows; each wave owns 16
 // rows (the 16 columns of the B operand) and every WK-th block of each K chunk
 // (WM*WK = 4).  Chunks of weights and activation fragments are staged through LDS
-// with the same register-prefetch pipeline as the VALU path; workgroups are
-// persistent over row tiles.  The WK partials of a tile are summed in LDS in wave
-// order at the end of its K walk.
+// with the same register-prefetch pipeline as the VALU path.  The WK partials of
+// a tile are summed in LDS in wave order at the end of its K walk.
+//
+// Scheduling: workgroups are persistent and take work items (a row tile, or
+// one K half of it) from a counter, largest first.  With whole tiles only, a
+// grid of ~3 workgroups per CU drew one or two 64-row tiles each and a quarter
+// of the chip idled for the last third of the launch; halves even this out.
+//
+// Weights are read with ordinary (not streaming) loads: a 64-row K chunk
+// starts and ends inside 128-byte lines, and the next chunk's loads find the
+// shared line in L2 only if it was not marked for early eviction.
+#include <algorithm>
+#include <climits>
+#include <map>
+#include <utility>
+
 #include "gemv_mfma_core.h"
 #include "ggq_launch.h"
 
@@ -16,20 +29,49 @@ namespace ggq {
 
 namespace {
 
+// A unit's position, with its job's fields copied in: they stay in scalar
+// registers, where reading them from the job table on every unit cost a
+// scalar-load round trip on the critical path.
 struct MPos {
-    int tile, job, chunk;
+    int job, chunk, cend;   // chunk: current K chunk; cend: one past the item's last
     int64_t r0;
+    const uint8_t* w;
+    uint8_t* xf;
+    float* y;
+    int64_t n, ldy;
+    uint32_t rb;
+    int k, nsplit;
 };
 
+// Work item -> (job, row tile, K range).  Items of a job are numbered tile by
+// tile, halves of a split tile next to each other; the first half takes the
+// odd chunk.
 template <int RWG>
-__device__ __forceinline__ MPos mlocate(const MJobs& jobs, int tile, int chunk) {
+__device__ __forceinline__ MPos mlocate(const MJobs& jobs, int item) {
     int j = 0;
-    while (j + 1 < jobs.count && tile >= jobs.j[j + 1].tile0) ++j;
+    while (j + 1 < jobs.count && item >= jobs.j[j + 1].item0) ++j;
+    const MJob& jb = jobs.j[j];
+    const int local = item - jb.item0;
     MPos p;
-    p.tile = tile;
     p.job = j;
-    p.chunk = chunk;
-    p.r0 = (int64_t)(tile - jobs.j[j].tile0) * RWG;
+    p.w = jb.w;
+    p.xf = jb.xf;
+    p.y = jb.y;
+    p.n = jb.n;
+    p.ldy = jb.ldy;
+    p.rb = (uint32_t)jb.rb;
+    p.k = jb.k;
+    p.nsplit = jb.nsplit;
+    if (jb.nsplit > 1) {
+        const int h0 = (jb.nchunk + 1) / 2;
+        p.r0 = (int64_t)(local >> 1) * RWG;
+        p.chunk = (local & 1) ? h0 : 0;
+        p.cend = (local & 1) ? jb.nchunk : h0;
+    } else {
+        p.r0 = (int64_t)local * RWG;
+        p.chunk = 0;
+        p.cend = jb.nchunk;
+    }
     return p;
 }
 
@@ -38,46 +80,84 @@ struct MPrefetch {
     using C = MCfg<FMT, MT, WM>;
     uint4 w[C::WP];
     uint4 f[C::FP];
+    // Per-thread piece offsets, set when the job changes, so that a unit's loads
+    // cost one add (or none) per piece: the unit's origin goes into the
+    // descriptor base instead.
+    uint32_t wrel[C::WP];    // weight piece: byte offset from the unit's first byte, kOob if none
+    uint32_t woff[C::WP];    // its byte offset inside the row chunk (partial last chunks)
+    uint32_t frel[C::FP];    // fragment piece: byte offset in the job region at chunk 0, kOob if none
+    uint32_t fpos[C::FP];    // Q4_K: position of its block in the chunk, in bytes of its kind
+    int job;
 
-    // Out-of-range pieces (rows past N, bytes past a row, blocks past K) load
-    // from an offset beyond the descriptor and come back as zeros.
-    __device__ __forceinline__ void load(const MJobs& jobs, const MPos& p, int tid) {
-        const MJob& jb = jobs.j[p.job];
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(jb.w, (uint32_t)(jb.n * jb.rb));
-        const uint32_t rb = (uint32_t)jb.rb;
-        const uint32_t cb0 = (uint32_t)p.chunk * C::CRB;
-        const uint32_t base = (uint32_t)p.r0 * rb + cb0;
+    __device__ __forceinline__ void set_job(const MPos& jb, int tid) {
+        const uint32_t rb = jb.rb;
 #pragma unroll
         for (int i = 0; i < C::WP; ++i) {
             const int q = tid + 256 * i;
             const uint32_t pr = (uint32_t)q / (C::CRB / 16);
-            const uint32_t off = ((uint32_t)q % (C::CRB / 16)) * 16;
-            const bool ok = q < C::WPIECES && cb0 + off < rb;
-            w[i] = buf_load16<true>(rw, ok ? base + pr * rb + off : kOob);
+            woff[i] = ((uint32_t)q % (C::CRB / 16)) * 16;
+            wrel[i] = q < C::WPIECES ? pr * rb + woff[i] : kOob;
         }
         const XfLayout L = xf_layout(FMT, jb.k, MT);
-        const __amdgpu_buffer_rsrc_t rf = make_rsrc(jb.xf, (uint32_t)L.bytes);
         const int nblk = jb.k / 32;
         const int nsb = jb.k / 256;
 #pragma unroll
         for (int i = 0; i < C::FP; ++i) {
             const int q = tid + 256 * i;
-            const int o = q * 16;  // byte offset inside this chunk's fragment staging
-            uint32_t src = kOob;
+            const int o = q * 16;  // byte offset inside a chunk's fragment staging
+            frel[i] = kOob;
+            fpos[i] = 0;
             if (q < C::FPIECES) {
                 if (o < C::kFrag) {
                     const int t = o / (C::NBLK * 1024);
                     const int rem = o % (C::NBLK * 1024);
-                    const int blk = p.chunk * C::NBLK + rem / 1024;
-                    if (blk < nblk)
-                        src = (uint32_t)(L.frag + ((int64_t)t * nblk + blk) * 1024 + rem % 1024);
+                    frel[i] = (uint32_t)(L.frag + (int64_t)t * nblk * 1024 + rem);
+                    fpos[i] = (uint32_t)(rem & ~1023);
                 } else if constexpr (FMT == kQ4_K) {
                     const int o2 = o - C::kFrag;
                     const int t = o2 / (C::NSB * 512);
                     const int rem = o2 % (C::NSB * 512);
-                    const int sb = p.chunk * C::NSB + rem / 512;
-                    if (sb < nsb) src = (uint32_t)(L.mins + ((int64_t)t * nsb + sb) * 512 + rem % 512);
+                    frel[i] = (uint32_t)(L.mins + (int64_t)t * nsb * 512 + rem);
+                    fpos[i] = (uint32_t)(rem & ~511);
                 }
+            }
+        }
+    }
+
+    // Out-of-range pieces (rows past N, bytes past a row, blocks past K) load
+    // from an offset beyond the descriptor and come back as zeros.
+    __device__ __forceinline__ void load(const MJobs& jobs, const MPos& p, int tid) {
+        const MPos& jb = p;
+        if (p.job != job) {
+            set_job(p, tid);
+            job = p.job;
+        }
+        const uint32_t rb = p.rb;
+        const uint32_t cb0 = (uint32_t)p.chunk * C::CRB;
+        const uint32_t base = (uint32_t)p.r0 * rb + cb0;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + base, (uint32_t)p.n * rb - base);
+#pragma unroll
+        for (int i = 0; i < C::WP; ++i) {
+            uint32_t src = wrel[i];
+            // Q8_0 chunks are always whole (K % 256 == 0 on this path)
+            if constexpr (FMT == kQ4_K) src = cb0 + woff[i] < rb ? src : kOob;
+            w[i] = buf_load16<false>(rw, src);
+        }
+        const __amdgpu_buffer_rsrc_t rf = make_rsrc(jb.xf, (uint32_t)xf_layout(FMT, jb.k, MT).bytes);
+#pragma unroll
+        for (int i = 0; i < C::FP; ++i) {
+            uint32_t src;
+            if constexpr (FMT == kQ8_0) {
+                src = frel[i] + (uint32_t)p.chunk * (C::NBLK * 1024);
+                if constexpr (C::FPIECES % 256 != 0) src = frel[i] == kOob ? kOob : src;
+            } else {
+                // fragment pieces advance NBLK blocks per chunk, min pieces NSB
+                // super-blocks; a piece past K (partial last chunk) loads zeros
+                const bool is_frag = tid + 256 * i < C::kFrag / 16;
+                const uint32_t step = is_frag ? C::NBLK * 1024 : C::NSB * 512;
+                const uint32_t lim = is_frag ? (uint32_t)jb.k * 32 : (uint32_t)jb.k * 2;
+                const uint32_t at = (uint32_t)p.chunk * step + fpos[i];
+                src = at < lim && frel[i] != kOob ? frel[i] + (uint32_t)p.chunk * step : kOob;
             }
             f[i] = buf_load16<false>(rf, src);
         }
@@ -102,25 +182,6 @@ struct MPrefetch {
 };
 
 // ---------------------------------------------------------------- main ----
-template <int RWG>
-__device__ __forceinline__ bool mnext(const MJobs& jobs, const MPos& p, MPos& q) {
-    if (p.chunk + 1 < jobs.j[p.job].nchunk) {
-        q = p;
-        q.chunk = p.chunk + 1;
-        return true;
-    }
-    // Workgroup b takes tile b in round 0, G-1-b in round 1, b in round 2, ...
-    // (G = grid size): with the longest jobs numbered first, the workgroups that
-    // drew a long tile in round 0 are the last to be served in round 1.
-    const int g = (int)gridDim.x;
-    const int r = p.tile / g;
-    const int b = (r & 1) ? g - 1 - p.tile % g : p.tile % g;
-    const int tn = (r + 1) * g + (((r + 1) & 1) ? g - 1 - b : b);
-    if (tn >= jobs.total_tiles) return false;
-    q = mlocate<RWG>(jobs, tn, 0);
-    return true;
-}
-
 // Compute one unit (chunk of a tile) from LDS; at the tile's last chunk, combine
 // the K-phase partials and store.
 template <int FMT, int MT, int WM>
@@ -129,10 +190,10 @@ __device__ __forceinline__ void mfma_unit(const MJobs& jobs, const MPos& cur, ui
                                           int j, int h, f32x4 (&acc)[MT]) {
     using C = MCfg<FMT, MT, WM>;
     constexpr int WK = C::WK;
-        const MJob& jb = jobs.j[cur.job];
+        const MPos& jb = cur;
         mfma_chunk<FMT, MT, WM>(lds, cur.chunk * C::KC, jb.k, lane, wm, wk, j, h, acc);
 
-        if (cur.chunk == jb.nchunk - 1) {
+        if (cur.chunk == cur.cend - 1) {
             // tile finished: sum the WK wave partials in wave order, then store
             if constexpr (WK > 1) {
                 float4* red = reinterpret_cast<float4*>(red_lds);
@@ -157,12 +218,21 @@ __device__ __forceinline__ void mfma_unit(const MJobs& jobs, const MPos& cur, ui
                 const int64_t row = cur.r0 + 16 * wm + j;
                 const float* inv = reinterpret_cast<const float*>(jb.xf + xf_layout(FMT, jb.k, MT).inv);
                 if (row < jb.n) {
+                    const bool split = jb.nsplit > 1;
 #pragma unroll
                     for (int t = 0; t < MT; ++t) {
                         // D rows 4h .. 4h+3 = (batch 8t + 2h, hi/lo), (batch 8t + 2h + 1, hi/lo)
                         const int b0 = 8 * t + 2 * h;
-                        if (b0 < batch) jb.y[(int64_t)b0 * jb.ldy + row] = (acc[t][0] + acc[t][1]) * inv[b0];
-                        if (b0 + 1 < batch) jb.y[(int64_t)(b0 + 1) * jb.ldy + row] = (acc[t][2] + acc[t][3]) * inv[b0 + 1];
+                        float* y0 = jb.y + (int64_t)b0 * jb.ldy + row;
+                        const float v0 = (acc[t][0] + acc[t][1]) * inv[b0];
+                        const float v1 = (acc[t][2] + acc[t][3]) * inv[b0 + 1];
+                        if (split) {
+                            if (b0 < batch) unsafeAtomicAdd(y0, v0);
+                            if (b0 + 1 < batch) unsafeAtomicAdd(y0 + jb.ldy, v1);
+                        } else {
+                            if (b0 < batch) *y0 = v0;
+                            if (b0 + 1 < batch) y0[jb.ldy] = v1;
+                        }
                     }
                 }
             }
@@ -183,12 +253,24 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const MJobs jobs, int ba
     const int j = lane & 15;    // B-operand column = W row within the wave's 16
     const int h = lane >> 4;    // k octet (16x16x32) / k quad (16x16x16)
 
-    if ((int)blockIdx.x >= jobs.total_tiles) return;
+    // Items are handed out largest first: item blockIdx.x, then whatever the
+    // work counter gives.  A workgroup asks the counter for its next item while
+    // prefetching the last unit of the current one, so an item goes to the
+    // workgroup that is about to be free; the answer passes through a two-slot
+    // LDS ring at the following barrier.
+    __shared__ int s_item[2];
+    const int g = (int)gridDim.x;
+    if ((int)blockIdx.x >= jobs.total_items) return;
     MPrefetch<FMT, MT, WM> pf;
-    MPos cur = mlocate<C::RWG>(jobs, blockIdx.x, 0);
+    pf.job = -1;
+    MPos cur = mlocate<C::RWG>(jobs, blockIdx.x);
     pf.load(jobs, cur, tid);
+    bool ask = cur.chunk + 1 == cur.cend;
+    if (ask && tid == 0) s_item[0] = g + atomicAdd(jobs.ctr, 1);
     pf.store(lds, tid);
     __syncthreads();
+    int qnext = ask ? s_item[0] : 0;   // next item; known once cur is its item's last unit
+    int qslot = 1;
 
     f32x4 acc[MT];
 #pragma unroll
@@ -199,14 +281,30 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const MJobs jobs, int ba
     int buf = 0;
     for (;;) {
         MPos nxt;
-        const bool more = mnext<C::RWG>(jobs, cur, nxt);
+        bool more = true;
+        if (cur.chunk + 1 < cur.cend) {
+            nxt = cur;
+            nxt.chunk = cur.chunk + 1;
+        } else if (qnext < jobs.total_items) {
+            nxt = mlocate<C::RWG>(jobs, qnext);
+        } else {
+            more = false;
+        }
+        ask = more && nxt.chunk + 1 == nxt.cend;
         if (more) pf.load(jobs, nxt, tid);
+        int got = 0;
+        if (ask && tid == 0) got = atomicAdd(jobs.ctr, 1);
         mfma_unit<FMT, MT, WM>(jobs, cur, lds + buf * C::kBuf, lds + 2 * C::kBuf, batch, lane, wm, wk,
                                j, h, acc);
         if (!more) break;
+        if (ask && tid == 0) s_item[qslot] = g + got;
         buf ^= 1;
         pf.store(lds + buf * C::kBuf, tid);
         __syncthreads();
+        if (ask) {
+            qnext = s_item[qslot];
+            qslot ^= 1;
+        }
         cur = nxt;
     }
 }
@@ -223,8 +321,27 @@ int device_cus() {
     return cus;
 }
 
+// Longest finishing time, in units, of items handed out largest first to g
+// workers that each take the next item when they finish one (list scheduling).
+// cls holds (units per item, item count) pairs sorted by units, largest first.
+int64_t list_makespan(const std::pair<int64_t, int64_t>* cls, int ncls, int64_t g) {
+    std::map<int64_t, int64_t> load;   // finishing time -> workers
+    load[0] = g;
+    for (int c = 0; c < ncls; ++c) {
+        int64_t rem = cls[c].second;
+        while (rem > 0) {
+            auto it = load.begin();
+            const int64_t at = it->first, m = it->second < rem ? it->second : rem;
+            if ((it->second -= m) == 0) load.erase(it);
+            load[at + cls[c].first] += m;
+            rem -= m;
+        }
+    }
+    return load.rbegin()->first;
+}
+
 template <int FMT, int MT, int WM>
-hipError_t launch_main(MJobs& jobs, int batch, hipStream_t s) {
+int mfma_blocks_per_cu() {
     using C = MCfg<FMT, MT, WM>;
     static int per_cu = 0;
     if (!per_cu) {
@@ -237,23 +354,74 @@ hipError_t launch_main(MJobs& jobs, int batch, hipStream_t s) {
             v = 1;
         per_cu = v;
     }
-    // number the tiles of the longest-K jobs first (stable order otherwise)
+    return per_cu;
+}
+
+// Plans the items (which jobs to cut into K halves: the choice with the
+// shortest list schedule, cutting only when it gains 3 %, the cost of zeroing
+// and adding the outputs), numbers them largest first, then launches the
+// activation split and the main kernel.
+template <int FMT, int MT, int WM>
+hipError_t launch_planned(MJobs& jobs, int batch, hipStream_t s) {
+    using C = MCfg<FMT, MT, WM>;
+    const int64_t slots = (int64_t)mfma_blocks_per_cu<FMT, MT, WM>() * device_cus();
+    int maxc = 0;
+    for (int i = 0; i < jobs.count; ++i) {
+        MJob& jb = jobs.j[i];
+        jb.nchunk = (jb.k + C::KC - 1) / C::KC;
+        jb.tiles = (int32_t)((jb.n + C::RWG - 1) / C::RWG);
+        maxc = jb.nchunk > maxc ? jb.nchunk : maxc;
+    }
+    // candidate cut thresholds: none, the longest jobs only, every job of 2+ chunks
+    const int cuts[3] = {INT_MAX, maxc, 2};
+    int best = INT_MAX;
+    int64_t best_t = 0;
+    for (int ci = 0; ci < 3; ++ci) {
+        const int cut = cuts[ci] < 2 ? 2 : cuts[ci];
+        std::pair<int64_t, int64_t> cls[kMaxJobs];
+        int64_t items = 0;
+        for (int i = 0; i < jobs.count; ++i) {
+            const MJob& jb = jobs.j[i];
+            const bool sp = jb.nchunk >= cut;
+            cls[i].first = sp ? (jb.nchunk + 1) / 2 : jb.nchunk;
+            cls[i].second = sp ? 2 * (int64_t)jb.tiles : jb.tiles;
+            items += cls[i].second;
+        }
+        std::sort(cls, cls + jobs.count,
+                  [](const std::pair<int64_t, int64_t>& a, const std::pair<int64_t, int64_t>& b) {
+                      return a.first > b.first;
+                  });
+        const int64_t t = list_makespan(cls, jobs.count, items < slots ? items : slots);
+        if (ci == 0 || t * 100 < best_t * 97) {
+            best = cut;
+            best_t = t;
+        }
+    }
+    for (int i = 0; i < jobs.count; ++i) jobs.j[i].nsplit = jobs.j[i].nchunk >= best ? 2 : 1;
+    // number the largest items first (stable otherwise)
+    auto units = [](const MJob& jb) { return jb.nsplit > 1 ? (jb.nchunk + 1) / 2 : jb.nchunk; };
     for (int i = 1; i < jobs.count; ++i)
-        for (int j = i; j > 0 && jobs.j[j].k > jobs.j[j - 1].k; --j) {
+        for (int j = i; j > 0 && units(jobs.j[j]) > units(jobs.j[j - 1]); --j) {
             const MJob t = jobs.j[j];
             jobs.j[j] = jobs.j[j - 1];
             jobs.j[j - 1] = t;
         }
     int total = 0;
+    int64_t kmax = 0;
     for (int i = 0; i < jobs.count; ++i) {
         MJob& jb = jobs.j[i];
-        jb.nchunk = (jb.k + C::KC - 1) / C::KC;
-        jb.tile0 = total;
-        jb.tiles = (int32_t)((jb.n + C::RWG - 1) / C::RWG);
-        total += jb.tiles;
+        jb.item0 = total;
+        total += jb.tiles * jb.nsplit;
+        kmax = jb.k > kmax ? jb.k : kmax;
     }
-    jobs.total_tiles = total;
-    const int64_t slots = (int64_t)per_cu * device_cus();
+    jobs.total_items = total;
+    jobs.ctr = reinterpret_cast<int32_t*>(jobs.j[0].xf + xf_layout(FMT, jobs.j[0].k, MT).ctrl);
+
+    const dim3 pgrid((unsigned)(jobs.count * MT * 8),
+                     (unsigned)((kmax / 32 + kXfragSlice - 1) / kXfragSlice));
+    hipLaunchKernelGGL(xfrag_kernel<FMT>, pgrid, dim3(256), 0, s, jobs, batch, MT);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     const unsigned grid = (unsigned)(total < slots ? total : slots);
     hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MT, WM>), dim3(grid), dim3(256), C::kLds, s, jobs,
                        batch);
@@ -266,8 +434,8 @@ hipError_t launch_mt(MJobs& jobs, int batch, hipStream_t s) {
     // otherwise 16 rows with K split over the four waves.
     int64_t rows = 0;
     for (int i = 0; i < jobs.count; ++i) rows += jobs.j[i].n;
-    if (rows >= 64 * 512) return launch_main<FMT, MT, 4>(jobs, batch, s);
-    return launch_main<FMT, MT, 1>(jobs, batch, s);
+    if (rows >= 64 * 512) return launch_planned<FMT, MT, 4>(jobs, batch, s);
+    return launch_planned<FMT, MT, 1>(jobs, batch, s);
 }
 
 }  // namespace
@@ -297,16 +465,6 @@ hipError_t launch_gemv_mfma(int type, const GemvDesc* descs, int count, int batc
         p += gemv_mfma_ws_bytes(type, d.k, batch);
     }
     if (jobs.count == 0) return hipSuccess;
-    int64_t kmax = 0;
-    for (int i = 0; i < jobs.count; ++i) kmax = jobs.j[i].k > kmax ? jobs.j[i].k : kmax;
-    const dim3 pgrid((unsigned)(jobs.count * mt * 8),
-                     (unsigned)((kmax / 32 + kXfragSlice - 1) / kXfragSlice));
-    if (type == kQ4_K)
-        hipLaunchKernelGGL(xfrag_kernel<kQ4_K>, pgrid, dim3(256), 0, s, jobs, batch, mt);
-    else
-        hipLaunchKernelGGL(xfrag_kernel<kQ8_0>, pgrid, dim3(256), 0, s, jobs, batch, mt);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     if (type == kQ4_K)
         return mt == 1 ? launch_mt<kQ4_K, 1>(jobs, batch, s) : launch_mt<kQ4_K, 2>(jobs, batch, s);
     return mt == 1 ? launch_mt<kQ8_0, 1>(jobs, batch, s) : launch_mt<kQ8_0, 2>(jobs, batch, s);

@@ -43,6 +43,7 @@ struct XfLayout {
     int64_t frag;   // [MT][K/32][64 lanes][8 fp16]
     int64_t mins;   // Q4_K: [MT][K/256][64 lanes][4 fp16]
     int64_t inv;    // [MT*8] fp32: 2^-S_b
+    int64_t ctrl;   // 256 bytes: the work counter of a grouped launch (first job's region)
     int64_t bytes;
 };
 
@@ -52,23 +53,28 @@ __host__ __device__ inline XfLayout xf_layout(int type, int64_t k, int mt) {
     L.mins = al256((int64_t)mt * (k / 32) * 1024);
     const int64_t mb = type == kQ4_K ? (int64_t)mt * (k / 256) * 512 : 0;
     L.inv = L.mins + al256(mb);
-    L.bytes = L.inv + al256((int64_t)mt * 8 * 4);   // 2^-S per padded row
+    L.ctrl = L.inv + al256((int64_t)mt * 8 * 4);    // 2^-S per padded row
+    L.bytes = L.ctrl + 256;
     return L;
 }
 
+// A job's work items are its row tiles, each whole or cut into two K halves
+// (nsplit 2).  The halves of a tile are added into y, which the pre-kernel
+// zeroes: two additions onto an exact zero give the same bits in either order.
 struct MJob {
     const uint8_t* w;
     const float* x;
     float* y;
     uint8_t* xf;      // this job's workspace region
     int64_t n, ldx, ldy, rb;
-    int32_t k, nchunk, tile0, tiles;
+    int32_t k, nchunk, item0, tiles, nsplit;
 };
 
 struct MJobs {
     MJob j[kMaxJobs];
+    int32_t* ctr;     // work counter (zeroed by the pre-kernel), or null
     int32_t count;
-    int32_t total_tiles;
+    int32_t total_items;
 };
 
 // ------------------------------------------------------------------ prep ----
@@ -89,6 +95,15 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
     const int tid = threadIdx.x;
     const bool live = b < batch;
     const float* xb = jb.x + (int64_t)(live ? b : 0) * jb.ldx;
+
+    // Outputs of split jobs are sums of two halves: start them at zero.  The
+    // slices of this (job, row) share the N rows between them.
+    if (jb.nsplit > 1 && live) {
+        const int64_t r0 = jb.n * slice / gridDim.y, r1 = jb.n * (slice + 1) / gridDim.y;
+        float* yb = jb.y + (int64_t)b * jb.ldy;
+        for (int64_t r = r0 + tid; r < r1; r += 256) yb[r] = 0.f;
+    }
+    if (jobs.ctr && blockIdx.x == 0 && slice == 0 && tid == 0) *jobs.ctr = 0;
 
     // max |x_b| -> scale 2^S with max * 2^S in [2^14, 2^15)
     __shared__ float red[4];
