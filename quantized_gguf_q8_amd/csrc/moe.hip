@@ -79,9 +79,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
     }
 }
 
-// One wave per token: top_k rounds of a wave-wide argmax (ties -> lower index),
-// then exp(l - l_max) over the selected logits, normalised in rank order.
-// kPer logits per lane: E <= 64*kPer.
+// One wave per token.  The top_k logits (ties -> lower index) are found by a
+// radix select over order-preserving 32-bit keys: 32 rounds, each counting
+// with wave ballots how many keys lie above a candidate threshold, so no
+// round waits on a cross-lane shuffle.  The selected entries are then ranked
+// against each other, and exp(l - l_max) over them is normalised in rank
+// order.  kPer logits per lane: E <= 64*kPer.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (v != v) return 0u;                  // NaN: below every number
+    if (v == 0.f) v = 0.f;                  // -0 and +0 are the same logit
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int ballot_count(bool c) {
+    return __builtin_popcountll(__ballot(c));
+}
+
 template <int kPer>
 __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restrict__ logits,
                                                           int64_t e, int top_k,
@@ -91,42 +105,61 @@ __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restric
     const int lane = threadIdx.x;
     const float* l = logits + ti * e;
     float v[kPer];
-    uint32_t taken = 0;
+    uint32_t key[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        int64_t i = (int64_t)j * 64 + lane;
+        const int64_t i = (int64_t)j * 64 + lane;
         v[j] = i < e ? l[i] : -__builtin_inff();
-        if (i >= e) taken |= 1u << j;
+        key[j] = i < e ? order_key(v[j]) : 0u;   // padding ranks below every logit
     }
+    // threshold = key of the top_k-th entry; `want` = how many entries equal to
+    // it are taken (the lowest indices among them)
+    uint32_t thr = 0, mask = 0;
+    int want = top_k;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        const uint32_t m = mask | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) cnt += ballot_count((key[j] & m) == cand);
+        if (cnt >= want) thr = cand;
+        else want -= cnt;
+        mask = m;
+    }
+    // compact the selected entries (index order) into LDS
+    __shared__ int cidx[kMaxTopK];
+    __shared__ uint32_t ckey[kMaxTopK];
+    __shared__ float cval[kMaxTopK];
     __shared__ int sel[kMaxTopK];
     __shared__ float selv[kMaxTopK];
-    for (int s = 0; s < top_k; ++s) {
-        float bv = -__builtin_inff();
-        int bi = 0x7FFFFFFF;
+    int base = 0, eq_before = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            int i = j * 64 + lane;
-            bool ok = !(taken >> j & 1u);
-            if (ok && (v[j] > bv || (v[j] == bv && i < bi))) {
-                bv = v[j];
-                bi = i;
-            }
+    for (int j = 0; j < kPer; ++j) {
+        const uint64_t eqm = __ballot(key[j] == thr);
+        const uint64_t below = (1ull << lane) - 1ull;   // lanes under this one
+        const bool tie_ok = key[j] == thr && eq_before + __builtin_popcountll(eqm & below) < want;
+        const bool take = key[j] > thr || tie_ok;
+        const uint64_t tm = __ballot(take);
+        if (take) {
+            const int pos = base + __builtin_popcountll(tm & below);
+            cidx[pos] = j * 64 + lane;
+            ckey[pos] = key[j];
+            cval[pos] = v[j];
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oi = __shfl_xor(bi, o, 64);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (bi == 0x7FFFFFFF) bi = 0;  // only non-finite logits left: defined, not meaningful
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == 0) {
-            sel[s] = bi;
-            selv[s] = bv;
-        }
+        base += __builtin_popcountll(tm);
+        eq_before += __builtin_popcountll(eqm);
+    }
+    __syncthreads();
+    // rank of entry `lane` among the selected: entries with a larger key, or an
+    // equal key and a lower index, come first
+    if (lane < top_k) {
+        const uint32_t mk = ckey[lane];
+        const int mi = cidx[lane];
+        int rank = 0;
+        for (int q = 0; q < top_k; ++q)
+            rank += (ckey[q] > mk || (ckey[q] == mk && cidx[q] < mi)) ? 1 : 0;
+        sel[rank] = mi;
+        selv[rank] = cval[lane];
     }
     __syncthreads();
     if (lane == 0) {
@@ -309,6 +342,48 @@ __device__ __forceinline__ MoeLists group_in_lds(const int32_t* __restrict__ idx
     int32_t* ix = list + p;
     int32_t* xr = ix + p;
     const int tid = threadIdx.x;
+    if (p <= 64) {
+        // One wave, one pair per lane, everything in registers: each lane
+        // compares its expert with every pair's (broadcast by readlane) to get
+        // its place in the (expert, pair) order, its expert's count and first
+        // slot, and the rank of its expert among the distinct ones.  Counts and
+        // offsets are written for active experts only, the only ones read.
+        if (tid < 64) {
+            const int lane = tid;
+            int ex = 0x7FFFFFFF;
+            if (lane < p) {
+                const int32_t v = idx[lane];
+                ex = (v < 0 || v >= e) ? 0 : v;
+            }
+            int less = 0, same_before = 0, same = 0;
+            for (int j = 0; j < p; ++j) {
+                const int exj = __builtin_amdgcn_readlane(ex, j);
+                less += exj < ex;
+                same_before += (exj == ex) & (j < lane);
+                same += exj == ex;
+            }
+            const bool first = lane < p && same_before == 0;
+            const uint64_t fm = __ballot(first);
+            int arank = 0;
+            for (int j = 0; j < p; ++j) {
+                const int exj = __builtin_amdgcn_readlane(ex, j);
+                arank += ((fm >> j) & 1ull) && exj < ex;
+            }
+            if (lane < p) {
+                const int pos = less + same_before;
+                list[pos] = lane;
+                xr[pos] = lane / xdiv;
+                if (first) {
+                    act[arank] = ex;
+                    cnt[ex] = same;
+                    off[ex] = less;
+                }
+            }
+            if (lane == 0) nact[0] = __builtin_popcountll(fm);
+        }
+        __syncthreads();
+        return MoeLists{cnt, off, act, list, xr, nact[0]};
+    }
     for (int i = tid; i < e; i += 256) cnt[i] = 0;
     for (int i = tid; i < p; i += 256) {
         int32_t ex = idx[i];

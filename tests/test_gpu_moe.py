@@ -79,6 +79,21 @@ def test_route_ties_and_edges(g):
     assert all(len(set(r)) == 32 for r in idxe)
 
 
+@pytest.mark.parametrize("e,k", [(200, 8), (300, 32), (1024, 17)])
+def test_route_many_experts(g, e, k):
+    """Expert counts past one and four logits per lane, with exact ties from
+    duplicated router rows and rounded activations."""
+    say(f"route e={e} k={k}")
+    h = 64
+    wr = synth.normal_f32((e, h), seed=2, tensor_id=7)
+    wr[e - 1] = wr[3]
+    wr[e // 2] = wr[3]
+    wr[e - 2] = 0.0
+    x = np.round(synth.normal_f32((5, h), seed=2, tensor_id=8) * 4) / 4
+    idx, _, _ = _route_checks(g, wr, x.astype(np.float32), k)
+    assert all(len(set(r)) == k for r in idx)
+
+
 def _moe_bound(fmt, mo, x, idx, probs, e, h, f):
     """First-order bound for the end-to-end expert layer (see module doc of
     oracle.moe): per-GEMV 1e-5 tolerances propagated through silu(g)*u."""
