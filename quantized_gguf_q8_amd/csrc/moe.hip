@@ -624,19 +624,22 @@ __device__ __forceinline__ void moe_compute(const MoeStage& st, const MoeUnit& u
     }
 }
 
-template <int FMT, int NB, int ROWS, int NMAT>
+// SINGLE: launched so that every workgroup computes one unit; LDS then holds
+// one W and one x buffer instead of two of each (pair lists follow them).
+template <int FMT, int NB, int ROWS, int NMAT, bool SINGLE>
 __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
     using C = MoeCfg<FMT, NB, ROWS, NMAT>;
     extern __shared__ __align__(16) uint8_t lds[];
     uint8_t* lw0 = lds;
-    uint8_t* lx0 = lds + 2 * C::kWBytes;
+    uint8_t* lx0 = lds + (SINGLE ? 1 : 2) * C::kWBytes;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = tid % C::SL;
     const int rl = tid / C::SL;
     MoeLists L;
     if (st.inline_group) {
-        L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lds + C::kLds));
+        uint8_t* lists = SINGLE ? lds + C::kWBytes + C::kXBuf : lds + C::kLds;
+        L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lists));
     } else {
         L = MoeLists{st.ws.cnt, st.ws.off, st.ws.active, st.ws.list, nullptr, st.ws.nact[0]};
     }
@@ -668,7 +671,10 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
         moe_compute<FMT, NB, ROWS, NMAT>(st, cur, lw0 + buf * C::kWBytes, lx0 + buf * C::kXBuf, s,
                                          rl, acc);
         if (!more) break;
-        buf ^= 1;
+        // With one buffer (more units than planned, e.g. an expert repeated in a
+        // token's slots) wait until every wave is done with it.
+        if constexpr (SINGLE) __syncthreads();
+        else buf ^= 1;
         pf.store_w(lw0 + buf * C::kWBytes, tid);
         pf.store_x(lx0 + buf * C::kXBuf, tid, min(NB, nxt.cnt - nxt.g0));
         __syncthreads();
@@ -917,45 +923,78 @@ int moe_device_cus() {
     return cus;
 }
 
+// Resident workgroups per compute unit of a stage kernel at an LDS size (the
+// last two sizes asked are cached).
+template <int FMT, int NB, int ROWS, int NMAT, bool SINGLE>
+int stage_blocks_per_cu(size_t lds) {
+    static size_t key[2] = {0, 0};
+    static int val[2] = {0, 0};
+    for (int i = 0; i < 2; ++i)
+        if (key[i] == lds) return val[i];
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_stream_kernel<FMT, NB, ROWS, NMAT, SINGLE>,
+                                                     256, lds) != hipSuccess || v <= 0)
+        v = 1;
+    key[1] = key[0];
+    val[1] = val[0];
+    key[0] = lds;
+    val[0] = v;
+    return v;
+}
+
+// `max_group`: the most tokens any expert can receive in this call.
 template <int FMT, int NB, int ROWS, int NMAT>
-hipError_t launch_stage(MoeStage st, int64_t slots, hipStream_t s) {
+hipError_t launch_stage(MoeStage st, int64_t slots, int64_t max_group, hipStream_t s) {
     using C = MoeCfg<FMT, NB, ROWS, NMAT>;
-    const size_t lds = C::kLds + (st.inline_group ? inline_group_bytes(st.e, st.p) : 0);
-    // resident workgroups per compute unit for this LDS size (cached for the
-    // last size asked)
-    static size_t per_cu_lds = 0;
-    static int per_cu = 0;
-    if (per_cu_lds != lds) {
-        int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_stream_kernel<FMT, NB, ROWS, NMAT>,
-                                                         256, lds) != hipSuccess || v <= 0)
-            v = 1;
-        per_cu = v;
-        per_cu_lds = lds;
-    }
+    const size_t lists = st.inline_group ? inline_group_bytes(st.e, st.p) : 0;
     st.nchunk = (st.k + C::KC - 1) / C::KC;
     st.tiles = (int32_t)((st.n + ROWS - 1) / ROWS);
     const int64_t most = slots * st.tiles;
+    // One unit per workgroup (a single K chunk, one token group, every tile
+    // resident at once): the second LDS buffer would never be used, and
+    // leaving it out lets more workgroups share a compute unit.  The kernel
+    // stays correct if a workgroup does get more units (it then reuses the one
+    // buffer behind a barrier).
+    if constexpr (NB == 1) {
+        const size_t lds1 = (size_t)C::kWBytes + C::kXBuf + lists;
+        const int64_t cap1 =
+            (int64_t)stage_blocks_per_cu<FMT, NB, ROWS, NMAT, true>(lds1) * moe_device_cus();
+        if (st.nchunk == 1 && max_group <= NB && most <= cap1) {
+            hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT, true>), dim3((unsigned)most),
+                               dim3(256), lds1, s, st);
+            return hipGetLastError();
+        }
+    }
+    const size_t lds = C::kLds + lists;
+    const int per_cu = stage_blocks_per_cu<FMT, NB, ROWS, NMAT, false>(lds);
     const int64_t cap = (int64_t)per_cu * moe_device_cus();
     const unsigned grid = (unsigned)(most < cap ? most : cap);
-    hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT>), dim3(grid), dim3(256), lds, s,
-                       st);
+    hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT, false>), dim3(grid), dim3(256), lds,
+                       s, st);
     return hipGetLastError();
 }
 
-// Rows per tile: the largest of 64/32/16 (at least 2*NB) that still gives every
-// compute unit two tiles when `slots` experts are active.
+// Rows per tile.  One token (NB = 1): the most rows whose K chunk covers the
+// whole row (8 rows for K <= 2048, 16 for K <= 1024), so a tile is one unit --
+// the stages are latency-bound there and a second chunk is a second round
+// trip.  Otherwise the largest of 64/32/16 (at least 2*NB) that still gives
+// every compute unit two tiles when `slots` experts are active.
 template <int FMT, int NB, int NMAT>
-hipError_t launch_stage_rows(const MoeStage& st, int64_t slots, hipStream_t s) {
+hipError_t launch_stage_rows(const MoeStage& st, int64_t slots, int64_t max_group,
+                             hipStream_t s) {
+    if constexpr (NB == 1) {
+        if (st.k <= 64 * (256 / 16)) return launch_stage<FMT, 1, 16, NMAT>(st, slots, max_group, s);
+        if (st.k <= 64 * (256 / 8)) return launch_stage<FMT, 1, 8, NMAT>(st, slots, max_group, s);
+    }
     const int64_t want = 2 * (int64_t)moe_device_cus();
     int rows = 64;
     while (rows > 16 && rows / 2 >= 2 * NB && slots * ((st.n + rows - 1) / rows) < want) rows /= 2;
-    if (rows == 64) return launch_stage<FMT, NB, 64, NMAT>(st, slots, s);
+    if (rows == 64) return launch_stage<FMT, NB, 64, NMAT>(st, slots, max_group, s);
     if constexpr (2 * NB <= 32)
-        if (rows == 32) return launch_stage<FMT, NB, 32, NMAT>(st, slots, s);
+        if (rows == 32) return launch_stage<FMT, NB, 32, NMAT>(st, slots, max_group, s);
     if constexpr (2 * NB <= 16)
-        if (rows == 16) return launch_stage<FMT, NB, 16, NMAT>(st, slots, s);
-    return launch_stage<FMT, NB, 32, NMAT>(st, slots, s);
+        if (rows == 16) return launch_stage<FMT, NB, 16, NMAT>(st, slots, max_group, s);
+    return launch_stage<FMT, NB, 32, NMAT>(st, slots, max_group, s);
 }
 
 template <int FMT, int NMAT>
@@ -1042,7 +1081,7 @@ hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8
     d.xdiv = 1;
     d.y = ws.dbuf;
     d.ws = ws;
-    return launch_stage_rows<FMT, 4, 1>(d, slots, s);
+    return launch_stage_rows<FMT, 4, 1>(d, slots, t, s);
 }
 
 template <int FMT, int NB>
@@ -1067,7 +1106,7 @@ hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* w
     a.xdiv = top_k;
     a.y = ws.hbuf;
     a.ws = ws;
-    hipError_t err = launch_stage_rows<FMT, NB, 2>(a, slots, s);
+    hipError_t err = launch_stage_rows<FMT, NB, 2>(a, slots, t, s);
     if (err != hipSuccess) return err;
     MoeStage d{};
     d.idx = idx;
@@ -1084,7 +1123,7 @@ hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* w
     d.xdiv = 1;
     d.y = ws.dbuf;
     d.ws = ws;
-    return launch_stage_rows<FMT, NB, 1>(d, slots, s);
+    return launch_stage_rows<FMT, NB, 1>(d, slots, t, s);
 }
 
 }  // namespace

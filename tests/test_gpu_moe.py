@@ -191,6 +191,22 @@ def test_moe_small_shapes(g, fmt, e, h, f, t, k):
     check_bound(y, yref, bound, "moe small")
 
 
+@pytest.mark.parametrize("fmt,t", [(Q4, 1), (Q8, 1), (Q4, 3)])
+def test_moe_repeated_expert_in_slots(g, fmt, t):
+    """A token whose slots name the same expert more than once (not produced by
+    moe_route, but valid input): every slot still counts once."""
+    say(f"moe repeated expert fmt={fmt} t={t}")
+    e, h, f, k = 10, 512, 768, 5
+    mo = _small(7, fmt, e, h, f, t)
+    idx = np.array([[4, 4, 7, 4, 1], [2, 2, 2, 2, 2], [9, 0, 9, 3, 0]][:t], dtype=np.int32)
+    probs = np.array([[0.3, 0.2, 0.25, 0.15, 0.1]] * t, dtype=np.float32)
+    y, _ = _run_moe(g, fmt, mo, idx, probs, e, h, f)
+    yref = oracle.moe(fmt, mo["wg"], mo["wu"], mo["wd"], e, h, f, mo["x"], idx,
+                      probs.astype(np.float64))
+    bound = _moe_bound(fmt, mo, mo["x"], idx, probs.astype(np.float64), e, h, f)
+    check_bound(y, yref, bound, "moe repeated expert")
+
+
 def test_moe_reads_only_selected_experts(g):
     """NaN scales in every unselected expert leave the output unchanged."""
     say("moe poison")
