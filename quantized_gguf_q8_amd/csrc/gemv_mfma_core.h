@@ -80,9 +80,12 @@ struct MJobs {
 // ------------------------------------------------------------------ prep ----
 // One workgroup per (job, padded batch row b).  Rows b >= batch write zeros so the
 // padded MFMA rows contribute nothing.
-// blockIdx.y splits K into slices of kXfragSlice blocks; every slice recomputes
-// the row's maximum (a cheap read of K floats) so the slices need no exchange.
-constexpr int kXfragSlice = 32;
+// blockIdx.y splits K into slices of kXfragSlice blocks (one slice up to K =
+// 16384).  A thread holds its pieces of the slice (8 floats each) in registers
+// from the single read that also gives the maximum; a row longer than one
+// slice is scanned once more for its maximum, so slices need no exchange.
+constexpr int kXfragPer = 8;                      // pieces per thread
+constexpr int kXfragSlice = 256 * kXfragPer / 4;  // 32-weight blocks per slice
 
 template <int FMT>
 __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch, int mt) {
@@ -105,17 +108,39 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
     }
     if (jobs.ctr && blockIdx.x == 0 && slice == 0 && tid == 0) *jobs.ctr = 0;
 
-    // max |x_b| -> scale 2^S with max * 2^S in [2^14, 2^15)
-    __shared__ float red[4];
+    const int nblk = k / 32;
+    const int q0 = slice * kXfragSlice * 4;             // first piece of the slice
+    const int q1 = min(nblk, (slice + 1) * kXfragSlice) * 4;
+    if (q0 >= nblk * 4) return;                          // this job's row is shorter
+    // piece q = (block q/4, octet q%4): 8 consecutive floats
+    float xv[kXfragPer][8];
     float m = 0.f;
-    if (live) {
+#pragma unroll
+    for (int i = 0; i < kXfragPer; ++i) {
+        const int q = q0 + tid + 256 * i;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) xv[i][c] = 0.f;
+        if (live && q < q1) {
+            const float4 a = *reinterpret_cast<const float4*>(xb + q * 8);
+            const float4 a2 = *reinterpret_cast<const float4*>(xb + q * 8 + 4);
+            xv[i][0] = a.x; xv[i][1] = a.y; xv[i][2] = a.z; xv[i][3] = a.w;
+            xv[i][4] = a2.x; xv[i][5] = a2.y; xv[i][6] = a2.z; xv[i][7] = a2.w;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(xv[i][c]));
+    }
+    if (live && gridDim.y > 1) {
+        // the rest of the row, for the row's maximum
         const float4* x4 = reinterpret_cast<const float4*>(xb);
-#pragma unroll 8
         for (int c = tid; c < k / 4; c += 256) {
+            if (c >= q0 * 2 && c < q1 * 2) continue;
             const float4 v = x4[c];
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         }
     }
+
+    // max |x_b| -> scale 2^S with max * 2^S in [2^14, 2^15)
+    __shared__ float red[4];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     if ((tid & 63) == 0) red[tid >> 6] = m;
@@ -135,23 +160,21 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
     // A-operand fragments of v_mfma_f32_16x16x32_f16: lane l = i + 16*h holds
     // A[i][8h .. 8h+7]; rows i = 2*bb (hi) and 2*bb + 1 (lo).
     _Float16* frag = reinterpret_cast<_Float16*>(jb.xf + L.frag);
-    const int nblk = k / 32;
-    const int q_end = min(nblk, (slice + 1) * kXfragSlice) * 4;
-    if (slice * kXfragSlice >= nblk) return;
-    for (int q = slice * kXfragSlice * 4 + tid; q < q_end; q += 256) {
+    _Float16* mins = reinterpret_cast<_Float16*>(jb.xf + L.mins);
+    const int nsb = k / 256;
+    const float sc5 = sc * (1.f / 32.f);
+#pragma unroll
+    for (int i = 0; i < kXfragPer; ++i) {
+        const int q = q0 + tid + 256 * i;
+        // a block's four pieces (four consecutive lanes) are all in or all out,
+        // which is all the sub-block sums below need from their shuffles
+        if (q >= q1) continue;
         const int blk = q >> 2;
         const int h = q & 3;
-        float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (live) {
-            const float4 a = *reinterpret_cast<const float4*>(xb + blk * 32 + 8 * h);
-            const float4 b2 = *reinterpret_cast<const float4*>(xb + blk * 32 + 8 * h + 4);
-            xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-            xv[4] = b2.x; xv[5] = b2.y; xv[6] = b2.z; xv[7] = b2.w;
-        }
         f16x8 hi, lo;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const float v = xv[c] * sc;
+            const float v = xv[i][c] * sc;
             const _Float16 vh = (_Float16)v;
             hi[c] = vh;
             lo[c] = (_Float16)(v - (float)vh);
@@ -159,37 +182,31 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
         _Float16* base = frag + ((int64_t)(t * nblk + blk) * 64) * 8;
         *reinterpret_cast<f16x8*>(base + (2 * bb + 16 * h) * 8) = hi;
         *reinterpret_cast<f16x8*>(base + (2 * bb + 1 + 16 * h) * 8) = lo;
-    }
-    if constexpr (FMT == kQ4_K) {
-        // A operand of v_mfma_f32_16x16x16_f16: lane l = i + 16*hq holds A[i][4hq .. 4hq+3].
-        // k = sub-block index 0..7 (hq 0, 1); hq 2, 3 are zero.
-        _Float16* mins = reinterpret_cast<_Float16*>(jb.xf + L.mins);
-        const int nsb = k / 256;
-        const float sc5 = sc * (1.f / 32.f);
-        // super-blocks whose sub-blocks start in this slice
-        const int sb0 = slice * kXfragSlice / 8, sb1 = min(nsb, (slice + 1) * kXfragSlice / 8);
-        for (int q = sb0 * 2 + tid; q < sb1 * 2; q += 256) {
-            const int sb = q >> 1;
-            const int hq = q & 1;
-            f16x4 hi, lo;
+        if constexpr (FMT == kQ4_K) {
+            // A operand of v_mfma_f32_16x16x16_f16: lane l = i + 16*hq holds
+            // A[i][4hq .. 4hq+3]; k = sub-block index 0..7 (hq 0, 1); hq 2, 3
+            // are zero.  Sub-block j of super-block sb is block 8*sb + j: its
+            // four pieces sit in four consecutive lanes.
+            float sblk = ((xv[i][0] + xv[i][1]) + (xv[i][2] + xv[i][3])) +
+                         ((xv[i][4] + xv[i][5]) + (xv[i][6] + xv[i][7]));
+            sblk += __shfl_xor(sblk, 1, 64);
+            sblk += __shfl_xor(sblk, 2, 64);
+            const int sb = blk >> 3;
+            const int j = blk & 7;
+            _Float16* mb = mins + ((int64_t)(t * nsb + sb) * 64) * 4;
+            if (h == 0) {
+                const float v = sblk * sc5;
+                const _Float16 vh = (_Float16)v;
+                const int hq = j >> 2, jj = j & 3;
+                mb[(2 * bb + 16 * hq) * 4 + jj] = vh;
+                mb[(2 * bb + 1 + 16 * hq) * 4 + jj] = (_Float16)(v - (float)vh);
+            } else if (h == 1 && j == 0) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 4 * hq + jj;
-                float s = 0.f;
-                if (live) {
-                    float p[4] = {0.f, 0.f, 0.f, 0.f};
-                    for (int c = 0; c < 32; ++c) p[c & 3] += xb[sb * 256 + j * 32 + c];
-                    s = ((p[0] + p[1]) + (p[2] + p[3])) * sc5;
+                for (int hq = 2; hq < 4; ++hq) {
+                    *reinterpret_cast<f16x4*>(mb + (2 * bb + 16 * hq) * 4) = f16x4{0, 0, 0, 0};
+                    *reinterpret_cast<f16x4*>(mb + (2 * bb + 1 + 16 * hq) * 4) = f16x4{0, 0, 0, 0};
                 }
-                const _Float16 sh = (_Float16)s;
-                hi[jj] = sh;
-                lo[jj] = (_Float16)(s - (float)sh);
             }
-            _Float16* base = mins + ((int64_t)(t * nsb + sb) * 64) * 4;
-            *reinterpret_cast<f16x4*>(base + (2 * bb + 16 * hq) * 4) = hi;
-            *reinterpret_cast<f16x4*>(base + (2 * bb + 1 + 16 * hq) * 4) = lo;
-            *reinterpret_cast<f16x4*>(base + (2 * bb + 16 * (hq + 2)) * 4) = f16x4{0, 0, 0, 0};
-            *reinterpret_cast<f16x4*>(base + (2 * bb + 1 + 16 * (hq + 2)) * 4) = f16x4{0, 0, 0, 0};
         }
     }
 }
