@@ -106,6 +106,16 @@ int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, in
  * descriptor of quant_gemv_grouped) at this batch; 0 on bad arguments. */
 size_t quant_gemv_workspace_size(int type, int64_t k, int batch);
 
+/* Larger workspace for a matrix of N rows and K columns: with at least this
+ * many bytes (summed over the descriptors of a grouped call) the matrix-core
+ * path may also cut each row tile into up to 16 K parts, run them on separate
+ * workgroups, keep their fp32 partial sums in the workspace and add them in
+ * part order in a second launch -- for short, long-K matrices, whose row tiles
+ * alone leave most of the chip idle.  The result is as deterministic and
+ * within the same tolerance as without.  With less (but at least
+ * quant_gemv_workspace_size) nothing changes.  0 on bad arguments. */
+size_t quant_gemv_split_workspace_size(int type, int64_t n, int64_t k, int batch);
+
 /*
  * quant_gemv_grouped -- several decode products of the same format and batch in
  * one launch: for each descriptor i,

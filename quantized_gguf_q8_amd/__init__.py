@@ -45,6 +45,7 @@ _SIGS = {
     "quant_dequantize": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "quant_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _P, _SZ, _P]),
     "quant_gemv_workspace_size": (_SZ, [_I, _I64, _I]),
+    "quant_gemv_split_workspace_size": (_SZ, [_I, _I64, _I64, _I]),
     "quant_gemv_grouped": (_I, [_I, _P, _I, _I, _P, _SZ, _P]),
     "quant_gemm_workspace_size": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "quant_gemm": (_I, [_I, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I, _P, _SZ, _P]),
@@ -125,8 +126,13 @@ def quant_gemv_workspace_size(fmt: int, k: int, batch: int) -> int:
     return _lib.quant_gemv_workspace_size(fmt, k, batch)
 
 
+def quant_gemv_split_workspace_size(fmt: int, n: int, k: int, batch: int) -> int:
+    return _lib.quant_gemv_split_workspace_size(fmt, n, k, batch)
+
+
 def _ws_arg(ws, need, device):
-    """None -> no workspace (vector-unit path); "auto" -> allocate; else a uint8 tensor."""
+    """None -> no workspace (vector-unit path); "auto" -> allocate `need` bytes;
+    else a uint8 tensor."""
     if ws is None:
         return None
     if isinstance(ws, str):
@@ -141,8 +147,10 @@ def quant_gemv(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
                y: torch.Tensor | None = None, ws=None) -> torch.Tensor:
     """y[b][r] = sum_c w[r][c] x[b][c]; x is [B, K] (B <= 16) or [K].
 
-    ws=None runs the fp32 vector-unit kernel; a workspace ("auto" or a uint8
-    tensor of quant_gemv_workspace_size bytes) lets batch >= 2 use the matrix cores."""
+    ws=None runs the fp32 vector-unit kernel; a workspace (a uint8 tensor of at
+    least quant_gemv_workspace_size bytes) lets batch >= 2 use the matrix cores;
+    "auto" allocates quant_gemv_split_workspace_size bytes, which also allows K
+    to be cut across workgroups."""
     _wbytes(w, fmt, n, k)
     squeeze = x.dim() == 1
     x2 = x.unsqueeze(0) if squeeze else x
@@ -153,7 +161,7 @@ def quant_gemv(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
     if y is None:
         y = torch.empty((b, n), dtype=torch.float32, device=w.device)
     _dev(y, "y", torch.float32)
-    wst = _ws_arg(ws, quant_gemv_workspace_size(fmt, k, b), w.device)
+    wst = _ws_arg(ws, quant_gemv_split_workspace_size(fmt, n, k, b), w.device)
     _ck("quant_gemv", _lib.quant_gemv(fmt, _ptr(w), n, k, _ptr(x2), k, _ptr(y), n, b, _ptr(wst),
                                       0 if wst is None else wst.numel(), _stream()))
     return y[0] if squeeze else y
@@ -196,7 +204,8 @@ class GemvGroup:
         self._ptr = ctypes.cast(self._arr, _P)
         self.count = len(items)
         self.weight_bytes = sum(n * row_bytes(fmt, k) for _, n, k, _, _ in items)
-        need = sum(quant_gemv_workspace_size(fmt, k, self.batch) for _, n, k, _, _ in items if n)
+        need = sum(quant_gemv_split_workspace_size(fmt, n, k, self.batch)
+                   for _, n, k, _, _ in items if n)
         self.ws = _ws_arg(ws, need, items[0][0].device)
         self._wsp = _ptr(self.ws)
         self._wsn = 0 if self.ws is None else self.ws.numel()

@@ -88,13 +88,22 @@ static size_t gemv_ws_need(int type, const ggq_gemv_desc* d, int count, int batc
     return need;
 }
 
+static size_t gemv_split_need(int type, const ggq_gemv_desc* d, int count, int batch) {
+    size_t need = 0;
+    for (int i = 0; i < count; ++i)
+        if (d[i].n > 0) need += ggq::gemv_split_ws_bytes(type, d[i].n, d[i].k, batch);
+    return need;
+}
+
 static int run_gemv(int type, const ggq_gemv_desc* d, int count, int batch, void* ws,
                     size_t ws_bytes, void* stream) {
     if (ws) {
         if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
         if (ws_bytes < gemv_ws_need(type, d, count, batch)) return GGQ_ERR_WORKSPACE;
+        const bool parts = ws_bytes >= gemv_split_need(type, d, count, batch);
         if (mfma_ok(type, d, count, batch))
-            return launched(ggq::launch_gemv_mfma(type, d, count, batch, ws, as_stream(stream)));
+            return launched(
+                ggq::launch_gemv_mfma(type, d, count, batch, ws, parts, as_stream(stream)));
     }
     return launched(ggq::launch_gemv_group(type, d, count, batch, as_stream(stream)));
 }
@@ -111,6 +120,12 @@ size_t quant_gemv_workspace_size(int type, int64_t k, int batch) {
     const int blk = block_of(type);
     if (!blk || k <= 0 || k % blk != 0 || batch < 1 || batch > kMaxBatch) return 0;
     return ggq::gemv_mfma_ws_bytes(type, k, batch);
+}
+
+size_t quant_gemv_split_workspace_size(int type, int64_t n, int64_t k, int batch) {
+    const size_t base = quant_gemv_workspace_size(type, k, batch);
+    if (!base || n < 0 || n > INT_MAX) return 0;
+    return ggq::gemv_split_ws_bytes(type, n, k, batch);
 }
 
 int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batch, void* ws,

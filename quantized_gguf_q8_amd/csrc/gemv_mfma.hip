@@ -10,9 +10,11 @@
 // a tile are summed in LDS in wave order at the end of its K walk.
 //
 // Scheduling: workgroups are persistent and take work items (a row tile, or
-// one K half of it) from a counter, largest first.  With whole tiles only, a
+// one of its K parts) from a counter, largest first.  With whole tiles only, a
 // grid of ~3 workgroups per CU drew one or two 64-row tiles each and a quarter
 // of the chip idled for the last third of the launch; halves even this out.
+// Short, long-K matrices (a few dozen row tiles) are cut into up to 16 K parts
+// when the workspace has room for their partial sums.
 //
 // Weights are read with ordinary (not streaming) loads: a 64-row K chunk
 // starts and ends inside 128-byte lines, and the next chunk's loads find the
@@ -37,10 +39,10 @@ struct MPos {
     int64_t r0;
     const uint8_t* w;
     uint8_t* xf;
-    float* y;
-    int64_t n, ldy;
+    float* out;             // where the item's results go: y, or its partial-sum plane
+    int64_t n, ostride;     // rows; distance between batch rows of `out`
     uint32_t rb;
-    int k, nsplit;
+    int k, add;             // add: atomic add into a zeroed y (one of two K halves)
 };
 
 // Work item -> (job, row tile, K range).  Items of a job are numbered tile by
@@ -56,17 +58,21 @@ __device__ __forceinline__ MPos mlocate(const MJobs& jobs, int item) {
     p.job = j;
     p.w = jb.w;
     p.xf = jb.xf;
-    p.y = jb.y;
     p.n = jb.n;
-    p.ldy = jb.ldy;
     p.rb = (uint32_t)jb.rb;
     p.k = jb.k;
-    p.nsplit = jb.nsplit;
+    p.out = jb.y;
+    p.ostride = jb.ldy;
+    p.add = jb.nsplit == 2;
     if (jb.nsplit > 1) {
-        const int h0 = (jb.nchunk + 1) / 2;
-        p.r0 = (int64_t)(local >> 1) * RWG;
-        p.chunk = (local & 1) ? h0 : 0;
-        p.cend = (local & 1) ? jb.nchunk : h0;
+        const int part = local % jb.nsplit;
+        p.r0 = (int64_t)(local / jb.nsplit) * RWG;
+        p.chunk = part * jb.cpp;
+        p.cend = min(jb.nchunk, p.chunk + jb.cpp);
+        if (jb.nsplit > 2) {
+            p.out = jb.part + (int64_t)part * jobs.batch * jb.n;
+            p.ostride = jb.n;
+        }
     } else {
         p.r0 = (int64_t)local * RWG;
         p.chunk = 0;
@@ -218,20 +224,19 @@ __device__ __forceinline__ void mfma_unit(const MJobs& jobs, const MPos& cur, ui
                 const int64_t row = cur.r0 + 16 * wm + j;
                 const float* inv = reinterpret_cast<const float*>(jb.xf + xf_layout(FMT, jb.k, MT).inv);
                 if (row < jb.n) {
-                    const bool split = jb.nsplit > 1;
 #pragma unroll
                     for (int t = 0; t < MT; ++t) {
                         // D rows 4h .. 4h+3 = (batch 8t + 2h, hi/lo), (batch 8t + 2h + 1, hi/lo)
                         const int b0 = 8 * t + 2 * h;
-                        float* y0 = jb.y + (int64_t)b0 * jb.ldy + row;
+                        float* y0 = jb.out + (int64_t)b0 * jb.ostride + row;
                         const float v0 = (acc[t][0] + acc[t][1]) * inv[b0];
                         const float v1 = (acc[t][2] + acc[t][3]) * inv[b0 + 1];
-                        if (split) {
+                        if (jb.add) {
                             if (b0 < batch) unsafeAtomicAdd(y0, v0);
-                            if (b0 + 1 < batch) unsafeAtomicAdd(y0 + jb.ldy, v1);
+                            if (b0 + 1 < batch) unsafeAtomicAdd(y0 + jb.ostride, v1);
                         } else {
                             if (b0 < batch) *y0 = v0;
-                            if (b0 + 1 < batch) y0[jb.ldy] = v1;
+                            if (b0 + 1 < batch) y0[jb.ostride] = v1;
                         }
                     }
                 }
@@ -357,64 +362,117 @@ int mfma_blocks_per_cu() {
     return per_cu;
 }
 
-// Plans the items (which jobs to cut into K halves: the choice with the
-// shortest list schedule, cutting only when it gains 3 %, the cost of zeroing
-// and adding the outputs), numbers them largest first, then launches the
-// activation split and the main kernel.
+// Sums the partial results of jobs cut into more than two K parts, in part
+// order: y[b][r] = part[0][b][r] + part[1][b][r] + ...
+__global__ __launch_bounds__(256) void parts_sum_kernel(const MJobs jobs, int batch) {
+    const MJob& jb = jobs.j[blockIdx.z];
+    const int b = blockIdx.y;
+    if (jb.nsplit <= 2 || b >= batch) return;
+    const int64_t plane = (int64_t)batch * jb.n;
+    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < jb.n;
+         r += (int64_t)gridDim.x * 256) {
+        const float* p = jb.part + (int64_t)b * jb.n + r;
+        float acc = p[0];
+        for (int q = 1; q < jb.nsplit; ++q) acc += p[q * plane];
+        jb.y[(int64_t)b * jb.ldy + r] = acc;
+    }
+}
+
+// Plans the items: how many K parts each job is cut into.  Candidates: whole
+// tiles; halves for the longest jobs; halves for every job of 2+ chunks; and,
+// with partial-sum space, parts of at most t chunks (up to kMaxParts) for t
+// from the even share of a workgroup downwards.  Each is scored by its list
+// schedule (largest items first, in units of one chunk); halves must gain 3 %
+// (zeroing y, the atomic adds) and deeper cuts one unit (the summing launch).
+// Items are then numbered
+// largest first and the activation split, main and (if needed) summing
+// kernels are launched.
 template <int FMT, int MT, int WM>
 hipError_t launch_planned(MJobs& jobs, int batch, hipStream_t s) {
     using C = MCfg<FMT, MT, WM>;
     const int64_t slots = (int64_t)mfma_blocks_per_cu<FMT, MT, WM>() * device_cus();
     int maxc = 0;
+    int64_t units = 0;
+    bool parts_ok = true;
     for (int i = 0; i < jobs.count; ++i) {
         MJob& jb = jobs.j[i];
         jb.nchunk = (jb.k + C::KC - 1) / C::KC;
         jb.tiles = (int32_t)((jb.n + C::RWG - 1) / C::RWG);
         maxc = jb.nchunk > maxc ? jb.nchunk : maxc;
+        units += (int64_t)jb.nchunk * jb.tiles;
+        parts_ok = parts_ok && jb.part != nullptr;
     }
-    // candidate cut thresholds: none, the longest jobs only, every job of 2+ chunks
-    const int cuts[3] = {INT_MAX, maxc, 2};
-    int best = INT_MAX;
-    int64_t best_t = 0;
-    for (int ci = 0; ci < 3; ++ci) {
-        const int cut = cuts[ci] < 2 ? 2 : cuts[ci];
+    // deep cuts: parts of at most `t` chunks, for t from about one
+    // workgroup's even share downwards
+    int64_t even = (units + slots - 1) / slots;
+    int targets[8];
+    int ntargets = 0;
+    if (parts_ok)
+        for (int64_t t = even; t >= 1 && ntargets < 8; t = t > 2 ? (t * 2) / 3 : t - 1)
+            targets[ntargets++] = (int)t;
+    auto parts_for = [&](int option, const MJob& jb) -> int {
+        if (jb.nchunk < 2) return 1;
+        if (option == 1) return jb.nchunk >= maxc ? 2 : 1;
+        if (option == 2) return 2;
+        if (option >= 3) {
+            const int t = targets[option - 3];
+            int p = (jb.nchunk + t - 1) / t;
+            p = p > kMaxParts ? kMaxParts : p;
+            const int cpp = (jb.nchunk + p - 1) / p;
+            return (jb.nchunk + cpp - 1) / cpp;   // no empty parts
+        }
+        return 1;
+    };
+    int best = 0;
+    int64_t best_cost = 0;
+    for (int option = 0; option < 3 + ntargets; ++option) {
         std::pair<int64_t, int64_t> cls[kMaxJobs];
         int64_t items = 0;
+        bool deep = false;
         for (int i = 0; i < jobs.count; ++i) {
             const MJob& jb = jobs.j[i];
-            const bool sp = jb.nchunk >= cut;
-            cls[i].first = sp ? (jb.nchunk + 1) / 2 : jb.nchunk;
-            cls[i].second = sp ? 2 * (int64_t)jb.tiles : jb.tiles;
+            const int p = parts_for(option, jb);
+            deep = deep || p > 2;
+            cls[i].first = (jb.nchunk + p - 1) / p;
+            cls[i].second = (int64_t)p * jb.tiles;
             items += cls[i].second;
         }
         std::sort(cls, cls + jobs.count,
                   [](const std::pair<int64_t, int64_t>& a, const std::pair<int64_t, int64_t>& b) {
                       return a.first > b.first;
                   });
-        const int64_t t = list_makespan(cls, jobs.count, items < slots ? items : slots);
-        if (ci == 0 || t * 100 < best_t * 97) {
-            best = cut;
-            best_t = t;
+        const int64_t cost =
+            100 * (list_makespan(cls, jobs.count, items < slots ? items : slots) + (deep ? 1 : 0));
+        if (option == 0 || cost < best_cost * 97 / 100) {
+            best = option;
+            best_cost = cost;
         }
     }
-    for (int i = 0; i < jobs.count; ++i) jobs.j[i].nsplit = jobs.j[i].nchunk >= best ? 2 : 1;
+    bool any_deep = false;
+    for (int i = 0; i < jobs.count; ++i) {
+        MJob& jb = jobs.j[i];
+        jb.nsplit = parts_for(best, jb);
+        jb.cpp = (jb.nchunk + jb.nsplit - 1) / jb.nsplit;
+        any_deep = any_deep || jb.nsplit > 2;
+    }
     // number the largest items first (stable otherwise)
-    auto units = [](const MJob& jb) { return jb.nsplit > 1 ? (jb.nchunk + 1) / 2 : jb.nchunk; };
     for (int i = 1; i < jobs.count; ++i)
-        for (int j = i; j > 0 && units(jobs.j[j]) > units(jobs.j[j - 1]); --j) {
+        for (int j = i; j > 0 && jobs.j[j].cpp > jobs.j[j - 1].cpp; --j) {
             const MJob t = jobs.j[j];
             jobs.j[j] = jobs.j[j - 1];
             jobs.j[j - 1] = t;
         }
     int total = 0;
-    int64_t kmax = 0;
+    int64_t kmax = 0, nmax = 0;
     for (int i = 0; i < jobs.count; ++i) {
         MJob& jb = jobs.j[i];
         jb.item0 = total;
         total += jb.tiles * jb.nsplit;
         kmax = jb.k > kmax ? jb.k : kmax;
+        nmax = jb.n > nmax ? jb.n : nmax;
     }
     jobs.total_items = total;
+    jobs.batch = batch;
     jobs.ctr = reinterpret_cast<int32_t*>(jobs.j[0].xf + xf_layout(FMT, jobs.j[0].k, MT).ctrl);
 
     const dim3 pgrid((unsigned)(jobs.count * MT * 8),
@@ -425,16 +483,28 @@ hipError_t launch_planned(MJobs& jobs, int batch, hipStream_t s) {
     const unsigned grid = (unsigned)(total < slots ? total : slots);
     hipLaunchKernelGGL((gemv_mfma_kernel<FMT, MT, WM>), dim3(grid), dim3(256), C::kLds, s, jobs,
                        batch);
+    err = hipGetLastError();
+    if (err != hipSuccess || !any_deep) return err;
+    const int64_t bx = (nmax + 255) / 256;
+    const dim3 sgrid((unsigned)(bx < 64 ? bx : 64), (unsigned)batch, (unsigned)jobs.count);
+    hipLaunchKernelGGL(parts_sum_kernel, sgrid, dim3(256), 0, s, jobs, batch);
     return hipGetLastError();
 }
 
 template <int FMT, int MT>
 hipError_t launch_mt(MJobs& jobs, int batch, hipStream_t s) {
-    // Rows per workgroup: 64 when there are enough row tiles to fill the chip,
-    // otherwise 16 rows with K split over the four waves.
+    // Rows per workgroup: 64, or 16 rows with K split over the four waves for
+    // short row counts at up to 8 activation rows and no partial-sum space.  A 16-row tile loads four
+    // times its weight bytes in activation fragments per chunk; it pays only
+    // when 64-row tiles would leave most of the chip idle and the fragments
+    // are small (one M tile).  Measured on Q4_K 9728x2560 / 2560x9728.
     int64_t rows = 0;
     for (int i = 0; i < jobs.count; ++i) rows += jobs.j[i].n;
-    if (rows >= 64 * 512) return launch_planned<FMT, MT, 4>(jobs, batch, s);
+    // With room for partial sums, K parts give the parallelism instead, and
+    // 64-row tiles are kept.
+    bool parts = true;
+    for (int i = 0; i < jobs.count; ++i) parts = parts && jobs.j[i].part != nullptr;
+    if (rows >= 8192 || MT > 1 || parts) return launch_planned<FMT, MT, 4>(jobs, batch, s);
     return launch_planned<FMT, MT, 1>(jobs, batch, s);
 }
 
@@ -444,8 +514,12 @@ size_t gemv_mfma_ws_bytes(int type, int64_t k, int batch) {
     return (size_t)xf_layout(type, k, (batch + 7) / 8).bytes;
 }
 
+size_t gemv_split_ws_bytes(int type, int64_t n, int64_t k, int batch) {
+    return gemv_mfma_ws_bytes(type, k, batch) + (size_t)al256((int64_t)kMaxParts * batch * n * 4);
+}
+
 hipError_t launch_gemv_mfma(int type, const GemvDesc* descs, int count, int batch, void* ws,
-                            hipStream_t s) {
+                            bool parts, hipStream_t s) {
     MJobs jobs{};
     const int mt = (batch + 7) / 8;
     uint8_t* p = static_cast<uint8_t*>(ws);
@@ -463,6 +537,10 @@ hipError_t launch_gemv_mfma(int type, const GemvDesc* descs, int count, int batc
         jb.rb = row_bytes(type, d.k);
         jb.k = (int32_t)d.k;
         p += gemv_mfma_ws_bytes(type, d.k, batch);
+        if (parts) {
+            jb.part = reinterpret_cast<float*>(p);
+            p += gemv_split_ws_bytes(type, d.n, d.k, batch) - gemv_mfma_ws_bytes(type, d.k, batch);
+        }
     }
     if (jobs.count == 0) return hipSuccess;
     if (type == kQ4_K)

@@ -58,16 +58,21 @@ __host__ __device__ inline XfLayout xf_layout(int type, int64_t k, int mt) {
     return L;
 }
 
-// A job's work items are its row tiles, each whole or cut into two K halves
-// (nsplit 2).  The halves of a tile are added into y, which the pre-kernel
-// zeroes: two additions onto an exact zero give the same bits in either order.
+// A job's work items are its row tiles, each whole or cut into nsplit K parts
+// of cpp chunks.  Two parts are added into y, which the pre-kernel zeroes: two
+// additions onto an exact zero give the same bits in either order.  More parts
+// write partial sums to `part` ([nsplit][batch][n] floats), which a second
+// kernel adds in part order.
+constexpr int kMaxParts = 16;
+
 struct MJob {
     const uint8_t* w;
     const float* x;
     float* y;
     uint8_t* xf;      // this job's workspace region
+    float* part;      // partial sums region (kMaxParts * batch * n floats), or null
     int64_t n, ldx, ldy, rb;
-    int32_t k, nchunk, item0, tiles, nsplit;
+    int32_t k, nchunk, item0, tiles, nsplit, cpp;
 };
 
 struct MJobs {
@@ -75,6 +80,7 @@ struct MJobs {
     int32_t* ctr;     // work counter (zeroed by the pre-kernel), or null
     int32_t count;
     int32_t total_items;
+    int32_t batch;    // activation rows (partial-sum plane height)
 };
 
 // ------------------------------------------------------------------ prep ----
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
 
     // Outputs of split jobs are sums of two halves: start them at zero.  The
     // slices of this (job, row) share the N rows between them.
-    if (jb.nsplit > 1 && live) {
+    if (jb.nsplit == 2 && live) {
         const int64_t r0 = jb.n * slice / gridDim.y, r1 = jb.n * (slice + 1) / gridDim.y;
         float* yb = jb.y + (int64_t)b * jb.ldy;
         for (int64_t r = r0 + tid; r < r1; r += 256) yb[r] = 0.f;

@@ -19,8 +19,11 @@ hipError_t launch_dequant(int type, const uint8_t* w, int64_t n, int64_t k, floa
 
 int gemv_max_group();
 size_t gemv_mfma_ws_bytes(int type, int64_t k, int batch);
+// With room for partial sums after each job's region, K may be cut into more
+// than two parts per tile (`parts`).
+size_t gemv_split_ws_bytes(int type, int64_t n, int64_t k, int batch);
 hipError_t launch_gemv_mfma(int type, const GemvDesc* descs, int count, int batch, void* ws,
-                            hipStream_t s);
+                            bool parts, hipStream_t s);
 hipError_t launch_gemv_group(int type, const GemvDesc* descs, int count, int batch, hipStream_t s);
 hipError_t launch_gemv(int type, const uint8_t* w, int64_t n, int64_t k, const float* x,
                        int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s);

@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("quant_gemv", "quant_gemm", "moe_expert_gemv", "moe_route", "quant_dequantize",
               "quant_gemm_workspace_size", "moe_workspace_size", "moe_workspace_h_offset",
+              "quant_gemv_workspace_size", "quant_gemv_split_workspace_size",
               "ggq_status_string", "ggq_version"):
         assert n in names
 
@@ -83,6 +84,11 @@ def test_gemv_workspace_validation(g):
     assert L.quant_gemv_workspace_size(12, 2560, 16) > L.quant_gemv_workspace_size(12, 2560, 8)
     assert L.quant_gemv(8, A16, 4, 2048, B16, 2048, C16, 4, 8, D16, need - 1, None) == WS
     assert L.quant_gemv(8, A16, 4, 2048, B16, 2048, C16, 4, 8, D16 + 16, need, None) == ALIGN
+    # the split-K workspace adds 16 partial planes of batch x N floats
+    S = L.quant_gemv_split_workspace_size
+    assert S(12, 2560, 9728, 4) >= L.quant_gemv_workspace_size(12, 9728, 4) + 16 * 4 * 2560 * 4
+    assert S(12, 0, 9728, 4) == L.quant_gemv_workspace_size(12, 9728, 4)
+    assert S(12, -1, 9728, 4) == 0 and S(12, 2560, 9700, 4) == 0 and S(8, 64, 2048, 17) == 0
 
 
 def test_gemv_grouped_validation(g):

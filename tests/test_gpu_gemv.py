@@ -123,6 +123,30 @@ def test_gemv_q4k_ffn_full_size(g, name, n, k, b, path):
     say(f"  worst err / bound = {worst:.3g}")
 
 
+@pytest.mark.parametrize("fmt,n,k,b", [
+    (Q4, 2560, 9728, 4),        # short and long-K: cut into many K parts
+    (Q4, 130, 11264, 16), (Q8, 96, 12288, 8), (Q8, 300, 6144, 3),
+])
+def test_gemv_split_workspace(g, fmt, n, k, b):
+    """The matrix-core path with the larger (split-K) workspace and with the
+    minimal one: both within tolerance, and the split result repeatable bit for
+    bit."""
+    say(f"gemv split ws fmt={fmt} n={n} k={k} b={b}")
+    w = synth.quant_matrix(fmt, n, k, seed=9, tensor_id=n + k)
+    x = synth.normal_f32((b, k), seed=9, tensor_id=n + k + 1)
+    wd, xd = dev(w), dev(x)
+    yr, s = oracle.gemv(fmt, w, n, k, x)
+    small = torch.empty(g.quant_gemv_workspace_size(fmt, k, b), dtype=torch.uint8, device="cuda")
+    big = torch.empty(g.quant_gemv_split_workspace_size(fmt, n, k, b), dtype=torch.uint8,
+                      device="cuda")
+    y1 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=small))
+    y2 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=big))
+    y3 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=big))
+    check_rel(y1, yr, s, GEMV_TOL, "minimal workspace")
+    check_rel(y2, yr, s, GEMV_TOL, "split workspace")
+    assert np.array_equal(y2, y3)
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_gemv_one_hot_columns_exact(g, path):
     """x = e_c gives the dequantized column c exactly (adds of zero are exact; on
