@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (HBM counter calibration)")
-    p.add_argument("--only", choices=["q4k", "moe", "gemm"], default=None,
+    p.add_argument("--only", choices=["q4k", "moe", "gemm", "sweep"], default=None,
                    help="run one secondary workload only (for profiling)")
     return p.parse_args()
 
@@ -346,6 +346,42 @@ def secondary(g, torch, synth, only=None):
                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del graphs, sets
         out["moe_q4k"] = res
+    if only in (None, "sweep"):
+        # Batch and prompt sweep on the Q4_K up projection: the decode GEMV
+        # (batch 1..16, matrix cores from 2) against the GEMM at M = batch, then
+        # the GEMM from just past the GEMV's 16 rows to pp2048.
+        res = {}
+        name, fmt, n, k = synth.PP512_GEMMS[0]
+        tid = synth.tid(4, n, k)
+        wh = synth.quant_matrix(fmt, n, k, seed=0, tensor_id=tid)
+        copies = max(2, -(-ROTATE_BYTES // wh.nbytes))
+        cps = [torch.from_numpy(wh).to(dev) for _ in range(copies)]
+        for m in (1, 4, 16, 17, 32, 64, 128, 256, 512, 1024, 2048):
+            a = torch.from_numpy(synth.normal_f32((m, k), 1, tid + m)).to(dev)
+            c = torch.empty((m, n), dtype=torch.float32, device=dev)
+            row = {}
+            if m <= 16:
+                calls = [g.GemvGroup(fmt, [(cw, n, k, a, c)], ws=None if m == 1 else "auto")
+                         for cw in cps]
+                graphs = capture(torch, [lambda: [call() for call in calls]])
+                ms = replay_ms(torch, graphs, 10, copies)
+                row["gemv_us"] = round(ms * 1e3, 2)
+                row["gemv_GB/s"] = round(wh.nbytes / (ms * 1e-3) / 1e9, 1)
+                del graphs, calls
+            wsg = torch.empty(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
+                              device=dev)
+            graphs = capture(torch, [lambda: [g.quant_gemm(fmt, cw, n, k, a, c, wsg)
+                                              for cw in cps]])
+            ms = replay_ms(torch, graphs, 10, copies)
+            tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            row["gemm_us"] = round(ms * 1e3, 2)
+            row["gemm_TFLOP/s"] = round(tflops, 1)
+            row["gemm_frac_bf16_peak"] = round(tflops / BF16_PEAK_TFLOPS, 4)
+            row["gemm_weight_GB/s"] = round(wh.nbytes / (ms * 1e-3) / 1e9, 1)
+            res[f"m{m}"] = row
+            del graphs, wsg
+        del cps
+        out["sweep_q4k_up"] = res
     if only in (None, "gemm"):
         res = {}
         m = synth.PP512_M

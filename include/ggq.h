@@ -144,7 +144,8 @@ int quant_gemv_grouped(int type, const ggq_gemv_desc *descs, int count, int batc
 
 /*
  * quant_gemm_workspace_size -- bytes of device workspace quant_gemm needs for
- * these sizes (the bf16 copy of A plus tile bookkeeping).  0 on bad arguments.
+ * these sizes (the bf16 copy of A plus tile bookkeeping; for M <= 16 at least
+ * the split-K GEMV workspace).  0 on bad arguments.
  */
 size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int mode);
 
@@ -153,7 +154,8 @@ size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int 
  *     c[i][r] = sum_c a[i][c] * w[r][c]   for i < M, r < N
  * Activations are rounded to bf16 and weight tiles decoded to bf16 in LDS; the
  * products accumulate in fp32 on the matrix cores.  Result within
- * 8e-3 * sum_c |a w| of the exact value.
+ * 8e-3 * sum_c |a w| of the exact value.  Up to 16 rows (M <= 16) the product
+ * runs as quant_gemv instead (one read of W; within its tighter 1e-5 bound).
  *   a     device fp32 [M][lda], lda >= K, lda % 4 == 0, 16-byte aligned
  *   c     device fp32 [M][ldc], ldc >= N
  *   mode  GGQ_GEMM_BF16

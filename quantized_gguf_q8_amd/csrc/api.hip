@@ -143,10 +143,24 @@ int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batc
     return run_gemv(type, descs, count, batch, ws, ws_bytes, stream);
 }
 
+// Up to 16 rows the GEMM runs as the batched decode GEMV (one read of W, no
+// padding of M to the GEMM's row tiles); its workspace must fit either path.
+constexpr int64_t kGemmViaGemvRows = 16;
+
+static size_t gemm_ws_need(int type, int64_t m, int64_t n, int64_t k) {
+    size_t need = ggq::gemm_workspace_bytes(type, m, n, k);
+    if (m >= 1 && m <= kGemmViaGemvRows) {
+        const size_t g = ggq::gemv_split_ws_bytes(type, n, k, (int)m);
+        need = g > need ? g : need;
+    }
+    return need;
+}
+
 size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int mode) {
     const int blk = block_of(type);
     if (!blk || mode != GGQ_GEMM_BF16 || m < 0 || n < 0 || k <= 0 || k % blk != 0) return 0;
-    return ggq::gemm_workspace_bytes(type, m, n, k);
+    if (n > (int64_t)INT_MAX || m > (int64_t)INT_MAX) return 0;
+    return gemm_ws_need(type, m, n, k);
 }
 
 int quant_gemm(int type, const void* w, int64_t n, int64_t k, const float* a, int64_t lda,
@@ -163,8 +177,13 @@ int quant_gemm(int type, const void* w, int64_t n, int64_t k, const float* a, in
     if (m == 0 || n == 0) return GGQ_OK;
     if (!w || !a || !c) return GGQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(a, 16) || lda % 4 != 0 || !aligned(c, 4)) return GGQ_ERR_ALIGN;
-    if (!ws || ws_bytes < ggq::gemm_workspace_bytes(type, m, n, k)) return GGQ_ERR_WORKSPACE;
+    if (!ws || ws_bytes < gemm_ws_need(type, m, n, k)) return GGQ_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+    if (m <= kGemmViaGemvRows) {
+        const ggq_gemv_desc d{w, n, k, a, lda, c, ldc};
+        if (check_gemv(type, d, (int)m) == GGQ_OK)
+            return run_gemv(type, &d, 1, (int)m, ws, ws_bytes, stream);
+    }
     return launched(ggq::launch_gemm(type, static_cast<const uint8_t*>(w), n, k, a, lda, m, c, ldc,
                                      ws, as_stream(stream)));
 }

@@ -390,6 +390,8 @@ Plan plan_for(int64_t m, int64_t n, int64_t k) {
     Plan best{4, 4, 64, 1, 1, 1};
     double best_t = 1e300;
     int64_t best_wgs = 0;
+    const double abytes = (double)mpad(m) * (double)kpad(k) * 2.0;
+    const double afill_w = abytes > 4.0 * (1 << 20) ? 0.5 : 0.1;
     const int wvs[] = {8, 4};
     const int nts[] = {6, 5, 4, 3, 2, 1};
     for (int wv : wvs) {
@@ -404,9 +406,17 @@ Plan plan_for(int64_t m, int64_t n, int64_t k) {
                     const int64_t kper = (ksteps + s - 1) / s;
                     const int64_t wgs = tiles_m * tn * s;
                     const int64_t rounds = (wgs + slots - 1) / slots;
-                    // cycles: 2048 MACs per CU-cycle at ~50% of peak; 2500 bytes per
-                    // cycle of memory for the partials (written and read back)
-                    double t = (double)rounds * (8 / wv) * (64.0 * wv) * bn * (kper * kBK) / 1024.0;
+                    // cycles per compute unit and round: 2048 MACs per cycle at ~50%
+                    // of peak, plus the cycles to bring the tile's real A rows in
+                    // at 64 bytes per cycle (each column tile re-reads its whole A
+                    // block, which narrow tiles pay for many times), counted at
+                    // 1/10 while the bf16 A fits one XCD's 4 MB L2 and at 1/2 when
+                    // it has to come from further out; 2500 bytes per cycle of
+                    // memory for split-K partials (written and read back)
+                    const double mfma = (8 / wv) * (64.0 * wv) * bn * (kper * kBK) / 1024.0;
+                    const double arows = (double)(mpad(m) < 64 * wv ? mpad(m) : 64 * wv);
+                    const double afill = (8 / wv) * arows * (kper * kBK) * 2.0 / 64.0;
+                    double t = (double)rounds * (mfma + afill_w * afill);
                     if (s > 1) t += (double)s * m * n * 8.0 / 2500.0;
                     if (t < best_t * 0.999 || (t <= best_t * 1.001 && wgs < best_wgs)) {
                         best_t = t;

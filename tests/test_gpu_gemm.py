@@ -59,6 +59,27 @@ def test_gemm_pp512_sampled(g, name, fmt, n, k):
     say(f"  worst err / bound (columns) = {worst:.3g}")
 
 
+@pytest.mark.parametrize("m", [17, 128, 2048])
+def test_gemm_prompt_sweep_sampled(g, m):
+    """Prompt lengths around pp512 (the GEMV / GEMM crossover just past the
+    GEMV's 16 rows, pp128, pp2048) on the Q4_K up projection: sampled rows x
+    all columns and all rows x sampled columns."""
+    name, fmt, n, k = synth.PP512_GEMMS[0]
+    say(f"gemm sweep {name} m={m}")
+    tid = synth.tid(4, n, k)
+    w = synth.quant_matrix(fmt, n, k, seed=0, tensor_id=tid)
+    a = synth.normal_f32((m, k), seed=1, tensor_id=tid + m)
+    c = host(g.quant_gemm(fmt, dev(w), n, k, dev(a)))
+    rng = np.random.default_rng(m)
+    rows = sorted(set(rng.choice(m, min(m, 14), replace=False).tolist()) | {0, m - 1})
+    cr, s = oracle.gemm(fmt, w, n, k, a[rows])
+    check_rel(c[rows], cr, s, GEMM_TOL, f"m={m} rows")
+    cols = sorted(set(rng.choice(n, 62, replace=False).tolist()) | {0, n - 1})
+    cc, ss = oracle.gemm_columns(fmt, w, n, k, a, cols)
+    worst = check_rel(c[:, cols], cc, ss, GEMM_TOL, f"m={m} columns")
+    say(f"  worst err / bound (columns) = {worst:.3g}")
+
+
 def test_gemm_single_row_matches_gemv_tolerance(g):
     say("gemm M=1 vs oracle gemv")
     for fmt, n, k in ((Q8, 256, 2048), (Q4, 256, 2560)):
