@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (HBM counter calibration)")
-    p.add_argument("--only", choices=["q4k", "moe", "gemm", "sweep"], default=None,
+    p.add_argument("--only", choices=["q4k", "moe", "ffn", "gemm", "sweep"], default=None,
                    help="run one secondary workload only (for profiling)")
     return p.parse_args()
 
@@ -346,6 +346,41 @@ def secondary(g, torch, synth, only=None):
                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del graphs, sets
         out["moe_q4k"] = res
+    if only in (None, "ffn"):
+        # Dense FFN gate/up of the ~1B layer set fused with SiLU*up
+        # (quant_gemv_swiglu) against the same two products as one grouped GEMV
+        # that writes g and u (the activation left to a later pass).
+        res = {}
+        n, k = next((n, k) for name, n, k in synth.DENSE_1B_LAYER_SET if name == "gate")
+        tid = synth.tid(1, n, k)
+        wgh = synth.q8_0_matrix(n, k, 0, tid)
+        wuh = synth.q8_0_matrix(n, k, 0, synth.tid(1, n, k) + 7)
+        pair = wgh.nbytes + wuh.nbytes
+        copies = max(2, -(-ROTATE_BYTES // pair))
+        cps = [(torch.from_numpy(wgh).to(dev), torch.from_numpy(wuh).to(dev)) for _ in range(copies)]
+        for b in (1, 8):
+            x = torch.from_numpy(synth.normal_f32((b, k), 0, tid + 1)).to(dev)
+            hh = torch.empty((b, n), dtype=torch.float32, device=dev)
+            yg = torch.empty((b, n), dtype=torch.float32, device=dev)
+            yu = torch.empty((b, n), dtype=torch.float32, device=dev)
+            ws = None if b == 1 else torch.empty(g.quant_gemv_workspace_size(g.Q8_0, k, b),
+                                                 dtype=torch.uint8, device=dev)
+            graphs = capture(torch, [lambda: [g.quant_gemv_swiglu(g.Q8_0, a_, u_, n, k, x, hh, ws)
+                                              for a_, u_ in cps]])
+            fused = replay_ms(torch, graphs, 10, copies)
+            del graphs
+            calls = [g.GemvGroup(g.Q8_0, [(a_, n, k, x, yg), (u_, n, k, x, yu)],
+                                 ws=None if b == 1 else "auto") for a_, u_ in cps]
+            graphs = capture(torch, [lambda: [c() for c in calls]])
+            grouped = replay_ms(torch, graphs, 10, copies)
+            del graphs, calls
+            res[f"gate_up_{n}x{k}_b{b}"] = {
+                "fused_us": round(fused * 1e3, 2),
+                "fused_GB/s": round(pair / (fused * 1e-3) / 1e9, 1),
+                "fused_frac_hbm": round(pair / (fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "grouped_two_gemv_us": round(grouped * 1e3, 2)}
+        del cps
+        out["ffn_swiglu_q8_0"] = res
     if only in (None, "sweep"):
         # Batch and prompt sweep on the Q4_K up projection: the decode GEMV
         # (batch 1..16, matrix cores from 2) against the GEMM at M = batch, then

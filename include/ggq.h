@@ -143,6 +143,30 @@ int quant_gemv_grouped(int type, const ggq_gemv_desc *descs, int count, int batc
                        size_t ws_bytes, void *stream);
 
 /*
+ * quant_gemv_swiglu -- the gate and up projections of a dense gated
+ * feed-forward in one pass, fused with its activation (README "Components":
+ * kernel fusion):
+ *     h[b][r] = silu(sum_c wg[r][c] x[b][c]) * (sum_c wu[r][c] x[b][c]),
+ *     silu(g) = g / (1 + exp(-g)),
+ * for b < batch, r < N -- the first half of a routed expert's feed-forward
+ * (moe_expert_gemv) for one expert and every token.  A workgroup holds the
+ * same rows of both matrices, so neither product is written out.  Each product
+ * is within the quant_gemv tolerance before the activation.
+ *   wg, wu  N x K quantized matrices, 16-byte aligned; K % 256 == 0
+ *   x       device fp32 [batch][ldx], 16-byte aligned, ldx % 4 == 0, ldx >= K
+ *   h       device fp32 [batch][ldh], ldh >= N
+ *   batch   1..16
+ *   ws      batch >= 2: device workspace of at least
+ *           quant_gemv_workspace_size(type, K, batch) bytes, 256-byte aligned
+ *           (the activation fragments); batch 1: may be NULL
+ * N == 0 is a no-op.  Errors: as quant_gemv; GGQ_ERR_ARG for K % 256 != 0;
+ * GGQ_ERR_WORKSPACE for batch >= 2 without the workspace.
+ */
+int quant_gemv_swiglu(int type, const void *wg, const void *wu, int64_t n, int64_t k,
+                      const float *x, int64_t ldx, float *h, int64_t ldh, int batch,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
  * quant_gemm_workspace_size -- bytes of device workspace quant_gemm needs for
  * these sizes (the bf16 copy of A plus tile bookkeeping; for M <= 16 at least
  * the split-K GEMV workspace).  0 on bad arguments.

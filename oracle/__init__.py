@@ -69,6 +69,8 @@ def lib():
         L.ggo_route_probs.argtypes = [P, I64, I64, P, I, P]
         L.ggo_expert_ffn.restype = I
         L.ggo_expert_ffn.argtypes = [I, P, P, P, I64, I64, I64, P, P, P, P, P, P, P, P]
+        L.ggo_gated_ffn.restype = I
+        L.ggo_gated_ffn.argtypes = [I, P, P, I64, I64, P, P, P, P, P, P]
         L.ggo_moe.restype = I
         L.ggo_moe.argtypes = [I, P, P, P, I64, I64, I64, P, I64, I64, P, P, I, P, P]
         L.ggo_gemm.restype = I
@@ -208,6 +210,22 @@ def expert_ffn(fmt: int, wg, wu, wd, e: int, hdim: int, f: int, x: np.ndarray):
     _check(lib().ggo_expert_ffn(fmt, _p(wg), _p(wu), _p(wd), e, hdim, f, _p(x),
                                 _p(out["g"]), _p(out["u"]), _p(out["sg"]), _p(out["su"]),
                                 _p(out["h"]), _p(out["y"]), _p(out["sy"])))
+    return out
+
+
+def gated_ffn(fmt: int, wg, wu, n: int, k: int, x: np.ndarray):
+    """Dense gated feed-forward, gate and up: dict of g, u, sg, su, h, each
+    [T][n] fp64, for the activation rows x [T][k]."""
+    wg, wu = (_c(a, np.uint8) for a in (wg, wu))
+    x = _c(np.atleast_2d(x), np.float32)
+    out = {name: np.empty((x.shape[0], n)) for name in ("g", "u", "sg", "su", "h")}
+    for t in range(x.shape[0]):
+        row = {name: np.empty(n) for name in out}
+        _check(lib().ggo_gated_ffn(fmt, _p(wg), _p(wu), n, k, _p(_c(x[t], np.float32)),
+                                   _p(row["g"]), _p(row["u"]), _p(row["sg"]), _p(row["su"]),
+                                   _p(row["h"])))
+        for name in out:
+            out[name][t] = row[name]
     return out
 
 

@@ -314,6 +314,21 @@ int ggo_expert_ffn(int fmt, const uint8_t *wg, const uint8_t *wu, const uint8_t 
     return rc;
 }
 
+/* Gate and up projections of a dense gated feed-forward on one token, fp64:
+ *   g = Wg x,  u = Wu x,  h = silu(g) * u with silu(g) = g / (1 + exp(-g))
+ * -- the first half of the expert feed-forward above, for Wg, Wu of n rows and
+ * k columns.  Outputs [n] each: g, u, sg = sum|Wg x|, su = sum|Wu x|, h. */
+int ggo_gated_ffn(int fmt, const uint8_t *wg, const uint8_t *wu, int64_t n, int64_t k,
+                  const float *x, double *g, double *u, double *sg, double *su, double *h)
+{
+    int rc = 0;
+    rc |= ggo_gemv(fmt, wg, n, k, x, k, 1, 0, n, g, sg, n);
+    rc |= ggo_gemv(fmt, wu, n, k, x, k, 1, 0, n, u, su, n);
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+    return rc;
+}
+
 /* Routed mixture-of-experts layer for tokens [t0, t1):
  *   y[t] = sum over the k selected experts of p[t][s] * (Wd[e] h_e(x[t]))
  * Only the selected experts' weights are read.  The sum runs over the selected

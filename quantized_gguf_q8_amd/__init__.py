@@ -47,6 +47,7 @@ _SIGS = {
     "quant_gemv_workspace_size": (_SZ, [_I, _I64, _I]),
     "quant_gemv_split_workspace_size": (_SZ, [_I, _I64, _I64, _I]),
     "quant_gemv_grouped": (_I, [_I, _P, _I, _I, _P, _SZ, _P]),
+    "quant_gemv_swiglu": (_I, [_I, _P, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _P, _SZ, _P]),
     "quant_gemm_workspace_size": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "quant_gemm": (_I, [_I, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I, _P, _SZ, _P]),
     "moe_route": (_I, [_P, _I64, _I64, _P, _I64, _I, _P, _P, _P, _P]),
@@ -165,6 +166,28 @@ def quant_gemv(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
     _ck("quant_gemv", _lib.quant_gemv(fmt, _ptr(w), n, k, _ptr(x2), k, _ptr(y), n, b, _ptr(wst),
                                       0 if wst is None else wst.numel(), _stream()))
     return y[0] if squeeze else y
+
+
+def quant_gemv_swiglu(fmt: int, wg: torch.Tensor, wu: torch.Tensor, n: int, k: int,
+                      x: torch.Tensor, h: torch.Tensor | None = None, ws="auto") -> torch.Tensor:
+    """h[b][r] = silu((Wg x)[b][r]) * (Wu x)[b][r] in one pass; x is [B, K] or [K].
+    ws: "auto", None (batch 1 only) or a uint8 tensor of quant_gemv_workspace_size."""
+    _wbytes(wg, fmt, n, k)
+    _wbytes(wu, fmt, n, k)
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    _dev(x2, "x", torch.float32)
+    if x2.shape[1] != k:
+        raise ValueError(f"x has {x2.shape[1]} columns, K = {k}")
+    b = x2.shape[0]
+    if h is None:
+        h = torch.empty((b, n), dtype=torch.float32, device=wg.device)
+    _dev(h, "h", torch.float32)
+    wst = _ws_arg(ws, quant_gemv_workspace_size(fmt, k, b), wg.device)
+    _ck("quant_gemv_swiglu", _lib.quant_gemv_swiglu(fmt, _ptr(wg), _ptr(wu), n, k, _ptr(x2), k,
+                                                    _ptr(h), n, b, _ptr(wst),
+                                                    0 if wst is None else wst.numel(), _stream()))
+    return h[0] if squeeze else h
 
 
 class GemvDesc(ctypes.Structure):

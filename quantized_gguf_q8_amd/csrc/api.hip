@@ -156,6 +156,25 @@ static size_t gemm_ws_need(int type, int64_t m, int64_t n, int64_t k) {
     return need;
 }
 
+int quant_gemv_swiglu(int type, const void* wg, const void* wu, int64_t n, int64_t k,
+                      const float* x, int64_t ldx, float* h, int64_t ldh, int batch, void* ws,
+                      size_t ws_bytes, void* stream) {
+    if (!block_of(type)) return GGQ_ERR_UNSUPPORTED;
+    const ggq_gemv_desc dg{wg, n, k, x, ldx, h, ldh}, du{wu, n, k, x, ldx, h, ldh};
+    int st = check_gemv(type, dg, batch);
+    if (st == GGQ_OK) st = check_gemv(type, du, batch);
+    if (st != GGQ_OK) return st;
+    if (k % 256 != 0) return GGQ_ERR_ARG;
+    if (n == 0) return GGQ_OK;
+    if (batch >= 2) {
+        if (!ws || ws_bytes < ggq::gemv_mfma_ws_bytes(type, k, batch)) return GGQ_ERR_WORKSPACE;
+        if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+    }
+    return launched(ggq::launch_swiglu(type, static_cast<const uint8_t*>(wg),
+                                       static_cast<const uint8_t*>(wu), n, k, x, ldx, h, ldh,
+                                       batch, ws, as_stream(stream)));
+}
+
 size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int mode) {
     const int blk = block_of(type);
     if (!blk || mode != GGQ_GEMM_BF16 || m < 0 || n < 0 || k <= 0 || k % blk != 0) return 0;

@@ -36,6 +36,10 @@ hipError_t launch_gemm(int type, const uint8_t* w, int64_t n, int64_t k, const f
 hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t,
                         int top_k, int32_t* idx, float* probs, float* logits, hipStream_t s);
 
+hipError_t launch_swiglu(int type, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t k,
+                         const float* x, int64_t ldx, float* h, int64_t ldh, int batch, void* ws,
+                         hipStream_t s);
+
 size_t moe_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f);
 size_t moe_ws_h_offset(int64_t e, int64_t t, int top_k);
 hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,

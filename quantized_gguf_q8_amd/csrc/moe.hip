@@ -303,12 +303,14 @@ struct MoeStage {
     int32_t k;             // weights per row
     int32_t nchunk;        // K chunks per row
     int32_t tiles;         // row tiles per expert
-    const float* x;        // activation rows, k floats each
-    int64_t xrows;
+    const float* x;        // activation rows, ldx floats apart
+    int64_t xrows, ldx;
     int32_t xdiv;          // activation row of pair p: p / xdiv
-    float* y;              // output row of pair p: y + p * n
+    float* y;              // output row of pair p: y + p * ldy
+    int64_t ldy;
     MoeWs ws;              // global lists (written by group_kernel) ...
-    const int32_t* idx;    // ... or, with inline_group, rebuilt in LDS from idx
+    const int32_t* idx;    // ... or, with inline_group, rebuilt in LDS from idx (null:
+                           // every pair to expert 0, the dense gated FFN)
     int32_t p, e;          // pairs, experts
     int32_t inline_group;
 };
@@ -352,7 +354,7 @@ __device__ __forceinline__ MoeLists group_in_lds(const int32_t* __restrict__ idx
             const int lane = tid;
             int ex = 0x7FFFFFFF;
             if (lane < p) {
-                const int32_t v = idx[lane];
+                const int32_t v = idx ? idx[lane] : 0;
                 ex = (v < 0 || v >= e) ? 0 : v;
             }
             int less = 0, same_before = 0, same = 0;
@@ -386,7 +388,7 @@ __device__ __forceinline__ MoeLists group_in_lds(const int32_t* __restrict__ idx
     }
     for (int i = tid; i < e; i += 256) cnt[i] = 0;
     for (int i = tid; i < p; i += 256) {
-        int32_t ex = idx[i];
+        int32_t ex = idx ? idx[i] : 0;
         ix[i] = (ex < 0 || ex >= e) ? 0 : ex;
     }
     __syncthreads();
@@ -502,7 +504,7 @@ struct MoePrefetch {
     }
 
     __device__ __forceinline__ void load_x(const MoeStage& st, const MoeUnit& u, int tid) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(st.x, (uint32_t)(st.xrows * st.k * 4));
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(st.x, (uint32_t)(st.xrows * st.ldx * 4));
         const int k0 = u.chunk * C::KC;
         const int batch = min(NB, u.cnt - u.g0);
 #pragma unroll
@@ -515,7 +517,7 @@ struct MoePrefetch {
             if (q < C::XPIECES && k0 + pos < st.k) {
                 const int64_t xr =
                     u.xrows ? u.xrows[u.g0 + b] : u.pairs[u.g0 + b] / st.xdiv;
-                off = (uint32_t)((xr * st.k + k0 + pos) * 4);
+                off = (uint32_t)((xr * st.ldx + k0 + pos) * 4);
             }
             x[i] = buf_load16<false>(r, off);
         }
@@ -613,7 +615,7 @@ __device__ __forceinline__ void moe_compute(const MoeStage& st, const MoeUnit& u
                         const float g = acc[0][b];
                         v = g / (1.0f + expf(-g)) * acc[1][b];
                     }
-                    st.y[(int64_t)u.pairs[u.g0 + b] * st.n + u.r0 + rl] = v;
+                    st.y[(int64_t)u.pairs[u.g0 + b] * st.ldy + u.r0 + rl] = v;
                 }
             }
         }
@@ -699,9 +701,10 @@ struct MoeMfma {
     const uint8_t* xf;     // fragments of the activation rows
     int32_t xmt;           // 8-row tiles in xf
     int32_t xdiv;          // activation row of pair p: p / xdiv
-    float* y;              // output row of pair p: y + p * n
+    float* y;              // output row of pair p: y + p * ldy
+    int64_t ldy;
     MoeWs ws;
-    const int32_t* idx;
+    const int32_t* idx;    // null: every pair to expert 0
     int32_t p, e, inline_group;
 };
 
@@ -870,15 +873,15 @@ __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
                 if (wave < 2 && r < st.n) {
                     const float u0 = red[(wave * 64 + lane) * 2], u1 = red[(wave * 64 + lane) * 2 + 1];
                     if (2 * h < batch)
-                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.n + r] = v0 / (1.0f + expf(-v0)) * u0;
+                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.ldy + r] = v0 / (1.0f + expf(-v0)) * u0;
                     if (2 * h + 1 < batch)
-                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.n + r] = v1 / (1.0f + expf(-v1)) * u1;
+                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.ldy + r] = v1 / (1.0f + expf(-v1)) * u1;
                 }
                 __syncthreads();
             } else {
                 if (r < st.n) {
-                    if (2 * h < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.n + r] = v0;
-                    if (2 * h + 1 < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.n + r] = v1;
+                    if (2 * h < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.ldy + r] = v0;
+                    if (2 * h + 1 < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.ldy + r] = v1;
                 }
             }
             acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1025,12 +1028,13 @@ hipError_t launch_mstage(MoeMfma st, int64_t slots, hipStream_t s) {
 
 // Split `rows` activation rows of K floats into the fragments at xf.
 template <int FMT>
-hipError_t launch_split(const float* x, int64_t rows, int64_t k, uint8_t* xf, hipStream_t s) {
+hipError_t launch_split(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* xf,
+                        hipStream_t s) {
     MJobs jobs{};
     jobs.count = 1;
     jobs.j[0].x = x;
     jobs.j[0].xf = xf;
-    jobs.j[0].ldx = k;
+    jobs.j[0].ldx = ldx;
     jobs.j[0].k = (int32_t)k;
     const int mt = (int)((rows + 7) / 8);
     const dim3 grid((unsigned)(mt * 8), (unsigned)((k / 32 + kXfragSlice - 1) / kXfragSlice));
@@ -1045,7 +1049,7 @@ hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8
     const int64_t p = t * top_k;
     const int64_t slots = p < e ? p : e;
     const bool inl = p <= kInlinePairs;
-    hipError_t err = launch_split<FMT>(x, t, hdim, ws.xfx, s);
+    hipError_t err = launch_split<FMT>(x, t, hdim, hdim, ws.xfx, s);
     if (err != hipSuccess) return err;
     MoeMfma a{};
     a.w[0] = wg;
@@ -1057,6 +1061,7 @@ hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8
     a.xmt = (int32_t)((t + 7) / 8);
     a.xdiv = top_k;
     a.y = ws.hbuf;
+    a.ldy = f;
     a.ws = ws;
     a.idx = idx;
     a.p = (int32_t)p;
@@ -1078,8 +1083,10 @@ hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8
     d.k = (int32_t)f;
     d.x = ws.hbuf;
     d.xrows = p;
+    d.ldx = f;
     d.xdiv = 1;
     d.y = ws.dbuf;
+    d.ldy = hdim;
     d.ws = ws;
     return launch_stage_rows<FMT, 4, 1>(d, slots, t, s);
 }
@@ -1103,8 +1110,10 @@ hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* w
     a.k = (int32_t)hdim;
     a.x = x;
     a.xrows = t;
+    a.ldx = hdim;
     a.xdiv = top_k;
     a.y = ws.hbuf;
+    a.ldy = f;
     a.ws = ws;
     hipError_t err = launch_stage_rows<FMT, NB, 2>(a, slots, t, s);
     if (err != hipSuccess) return err;
@@ -1120,8 +1129,10 @@ hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* w
     d.k = (int32_t)f;
     d.x = ws.hbuf;
     d.xrows = p;
+    d.ldx = f;
     d.xdiv = 1;
     d.y = ws.dbuf;
+    d.ldy = hdim;
     d.ws = ws;
     return launch_stage_rows<FMT, NB, 1>(d, slots, t, s);
 }
@@ -1146,6 +1157,55 @@ hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, i
         hipLaunchKernelGGL((topk_softmax_kernel<16>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
                            top_k, idx, probs);
     return hipGetLastError();
+}
+
+// The gate and up projections of a dense gated FFN with the SiLU*up epilogue:
+// the expert stages with one expert that every token is routed to.
+hipError_t launch_swiglu(int type, const uint8_t* wg, const uint8_t* wu, int64_t n, int64_t k,
+                         const float* x, int64_t ldx, float* h, int64_t ldh, int batch, void* ws,
+                         hipStream_t s) {
+    const bool q4 = type == kQ4_K;
+    const int64_t rb = row_bytes(type, k);
+    if (batch <= 1) {
+        MoeStage a{};
+        a.idx = nullptr;
+        a.p = batch;
+        a.e = 1;
+        a.inline_group = 1;
+        a.w[0] = wg;
+        a.w[1] = wu;
+        a.n = n;
+        a.rb = rb;
+        a.k = (int32_t)k;
+        a.x = x;
+        a.xrows = batch;
+        a.ldx = ldx;
+        a.xdiv = 1;
+        a.y = h;
+        a.ldy = ldh;
+        return q4 ? launch_stage_rows<kQ4_K, 1, 2>(a, 1, 1, s)
+                  : launch_stage_rows<kQ8_0, 1, 2>(a, 1, 1, s);
+    }
+    uint8_t* xf = static_cast<uint8_t*>(ws);
+    hipError_t err = q4 ? launch_split<kQ4_K>(x, batch, k, ldx, xf, s)
+                        : launch_split<kQ8_0>(x, batch, k, ldx, xf, s);
+    if (err != hipSuccess) return err;
+    MoeMfma a{};
+    a.w[0] = wg;
+    a.w[1] = wu;
+    a.n = n;
+    a.rb = rb;
+    a.k = (int32_t)k;
+    a.xf = xf;
+    a.xmt = (int32_t)((batch + 7) / 8);
+    a.xdiv = 1;
+    a.y = h;
+    a.ldy = ldh;
+    a.idx = nullptr;
+    a.p = batch;
+    a.e = 1;
+    a.inline_group = 1;
+    return q4 ? launch_mstage<kQ4_K, 2>(a, 1, s) : launch_mstage<kQ8_0, 2>(a, 1, s);
 }
 
 size_t moe_ws_h_offset(int64_t e, int64_t t, int top_k) { return ints_bytes(e, t * top_k); }

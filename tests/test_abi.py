@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     for n in ("quant_gemv", "quant_gemm", "moe_expert_gemv", "moe_route", "quant_dequantize",
               "quant_gemm_workspace_size", "moe_workspace_size", "moe_workspace_h_offset",
               "quant_gemv_workspace_size", "quant_gemv_split_workspace_size",
+              "quant_gemv_swiglu",
               "ggq_status_string", "ggq_version"):
         assert n in names
 
@@ -89,6 +90,21 @@ def test_gemv_workspace_validation(g):
     assert S(12, 2560, 9728, 4) >= L.quant_gemv_workspace_size(12, 9728, 4) + 16 * 4 * 2560 * 4
     assert S(12, 0, 9728, 4) == L.quant_gemv_workspace_size(12, 9728, 4)
     assert S(12, -1, 9728, 4) == 0 and S(12, 2560, 9700, 4) == 0 and S(8, 64, 2048, 17) == 0
+
+
+def test_gemv_swiglu_validation(g):
+    L = g._lib
+    f = L.quant_gemv_swiglu
+    assert f(5, A16, A16, 4, 2048, B16, 2048, C16, 4, 1, None, 0, None) == UNSUP
+    assert f(8, A16, A16, 4, 2080, B16, 2080, C16, 4, 1, None, 0, None) == ARG   # K % 256
+    assert f(8, A16, A16, 4, 2048, B16, 2048, C16, 4, 17, None, 0, None) == ARG  # batch
+    assert f(8, A16, A16, 4, 2048, B16, 2047, C16, 4, 1, None, 0, None) == ARG   # ldx < K
+    assert f(8, A16, A16 + 4, 4, 2048, B16, 2048, C16, 4, 1, None, 0, None) == ALIGN
+    need = L.quant_gemv_workspace_size(8, 2048, 4)
+    assert f(8, A16, A16, 4, 2048, B16, 2048, C16, 4, 4, None, 0, None) == WS
+    assert f(8, A16, A16, 4, 2048, B16, 2048, C16, 4, 4, D16, need - 1, None) == WS
+    assert f(8, A16, A16, 4, 2048, B16, 2048, C16, 4, 4, D16 + 16, need, None) == ALIGN
+    assert f(8, None, None, 0, 2048, None, 2048, None, 0, 4, None, 0, None) == OK  # N = 0
 
 
 def test_gemv_grouped_validation(g):

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from _gpu import GEMV_TOL, check_rel, dev, host, say
+from _gpu import GEMV_TOL, check_bound, check_rel, dev, host, say
 from _golden import q4_k_blocks, q8_0_blocks
 
 pytestmark = [pytest.mark.gpu,
@@ -145,6 +145,62 @@ def test_gemv_split_workspace(g, fmt, n, k, b):
     check_rel(y1, yr, s, GEMV_TOL, "minimal workspace")
     check_rel(y2, yr, s, GEMV_TOL, "split workspace")
     assert np.array_equal(y2, y3)
+
+
+# --------------------------------------------------------------------------- #
+# fused gate/up with SiLU * up (dense gated feed-forward)
+def _swiglu_bound(o):
+    """Per-element bound for h = silu(g) * u from the per-product GEMV
+    tolerances (first order; |d silu / dg| <= 1.1) plus fp32 rounding."""
+    sig = 1.0 / (1.0 + np.exp(-o["g"]))
+    return (1.1 * np.abs(o["u"]) * GEMV_TOL * o["sg"] + np.abs(o["g"] * sig) * GEMV_TOL * o["su"]
+            + 1e-6 * np.abs(o["h"]))
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [
+    (Q8, 6144, 2048, 1), (Q8, 6144, 2048, 8),          # the ~1B layer set's gate/up
+    (Q4, 9728, 2560, 1), (Q4, 9728, 2560, 4), (Q4, 9728, 2560, 16),
+    (Q8, 100, 512, 3), (Q4, 77, 768, 1), (Q8, 33, 4096, 16), (Q4, 300, 256, 9),
+])
+def test_gemv_swiglu(g, fmt, n, k, b):
+    say(f"swiglu fmt={fmt} n={n} k={k} b={b}")
+    wg = synth.quant_matrix(fmt, n, k, seed=5, tensor_id=3 * n + k)
+    wu = synth.quant_matrix(fmt, n, k, seed=5, tensor_id=3 * n + k + 1)
+    x = synth.normal_f32((b, k), seed=5, tensor_id=3 * n + k + 2)
+    h = host(g.quant_gemv_swiglu(fmt, dev(wg), dev(wu), n, k, dev(x)))
+    o = oracle.gated_ffn(fmt, wg, wu, n, k, x)
+    worst = check_bound(h, o["h"], _swiglu_bound(o), "swiglu")
+    say(f"  worst err / bound = {worst:.3g}")
+
+
+def test_gemv_swiglu_strided_and_repeatable(g):
+    """Row strides of x and h larger than K and N (through the C ABI), and the
+    same bits on a second call."""
+    import ctypes
+    for fmt, n, k, b in ((Q4, 260, 1024, 5), (Q8, 130, 2048, 1)):
+        wg = synth.quant_matrix(fmt, n, k, seed=6, tensor_id=n)
+        wu = synth.quant_matrix(fmt, n, k, seed=6, tensor_id=n + 1)
+        x = synth.normal_f32((b, k), seed=6, tensor_id=n + 2)
+        ldx, ldh = k + 64, n + 12
+        xp = torch.zeros((b, ldx), dtype=torch.float32, device="cuda")
+        xp[:, :k] = dev(x)
+        hp = torch.full((b, ldh), 7.0, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(g.quant_gemv_workspace_size(fmt, k, b), 256), dtype=torch.uint8,
+                         device="cuda")
+        wgd, wud = dev(wg), dev(wu)
+        def call():
+            rc = g._lib.quant_gemv_swiglu(fmt, wgd.data_ptr(), wud.data_ptr(), n, k,
+                                          xp.data_ptr(), ldx, hp.data_ptr(), ldh, b,
+                                          ws.data_ptr(), ws.numel(), None)
+            assert rc == 0, rc
+            torch.cuda.synchronize()
+            return host(hp).copy()
+        h1 = call()
+        h2 = call()
+        assert np.array_equal(h1, h2)
+        assert np.all(h1[:, n:] == 7.0)        # the padding columns are not written
+        o = oracle.gated_ffn(fmt, wg, wu, n, k, x)
+        check_bound(h1[:, :n], o["h"], _swiglu_bound(o), "swiglu strided")
 
 
 @pytest.mark.parametrize("path", PATHS)

@@ -220,6 +220,44 @@ def test_moe_expert_ffn_against_numpy(orc):
         assert np.allclose(out["y"], yy, rtol=0, atol=1e-12 * out["sy"].max())
 
 
+def test_gated_ffn_silu_invariants(orc):
+    """Dense gate/up pins that do not restate the formula: with x = e_0 and
+    d = 1, row r of each matrix gives its q[0] exactly, so
+      * g = 0 gives h = 0 exactly,
+      * rows with gate values v and -v and u = 1 differ by exactly v
+        (silu(v) - silu(-v) = v, since the logistic function has
+        sigma(v) + sigma(-v) = 1),
+      * u scales h linearly (u = 3 gives three times the u = 1 value)."""
+    n, k = 8, 64
+    v = np.array([0, 5, -5, 17, -17, 1, -1, 100], dtype=np.int64)
+    qg = np.zeros((n, k), dtype=np.int64)
+    qg[:, 0] = v
+    qu = np.zeros((n, k), dtype=np.int64)
+    qu[:, 0] = [1, 1, 1, 1, 1, 3, 1, 1]
+    wg = _q8_blocks_with(n, k, 0x3C00, qg)
+    wu = _q8_blocks_with(n, k, 0x3C00, qu)
+    x = np.zeros((1, k), dtype=np.float32)
+    x[0, 0] = 1.0
+    out = orc.gated_ffn(Q8, wg, wu, n, k, x)
+    assert np.array_equal(out["g"][0], v.astype(np.float64))
+    h = out["h"][0]
+    assert h[0] == 0.0
+    assert abs((h[1] - h[2]) - 5.0) <= 1e-14 * 5
+    assert abs((h[3] - h[4]) - 17.0) <= 1e-14 * 17
+    assert abs(h[5] - 3.0 * (h[6] + 1.0)) <= 1e-14   # silu(1) = 1 + silu(-1)
+    assert abs(h[7] - 100.0) < 1e-40 + 100.0 * np.exp(-99.0)
+
+
+def test_gated_ffn_equals_expert_ffn_first_half(orc):
+    """The dense gate/up is the routed expert's first half for one expert."""
+    _, wg, wu, wd, x = _small_moe(seed=3, e=2, h=512, f=256, t=2)
+    for t in range(2):
+        out = orc.gated_ffn(Q4, wg[1], wu[1], 256, 512, x[t])
+        ref = orc.expert_ffn(Q4, wg, wu, wd, 1, 512, 256, x[t])
+        for name in ("g", "u", "sg", "su", "h"):
+            assert np.array_equal(out[name][0], ref[name])
+
+
 def test_moe_reads_only_the_selected_experts(orc):
     """Poisoning every unselected expert's bytes (NaN scales) leaves y unchanged."""
     e, h, f, k = 6, 256, 256, 2
