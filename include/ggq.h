@@ -245,6 +245,41 @@ int moe_expert_gemv(int type, const void *wg, const void *wu, const void *wd, in
 /* Byte offset of the hidden-state array h inside the moe_expert_gemv workspace. */
 size_t moe_workspace_h_offset(int64_t e, int64_t t, int top_k);
 
+/*
+ * moe_gemm_workspace_size -- device workspace bytes moe_expert_gemm needs:
+ * per-expert slot lists and tiles, x in bf16, h in bf16 (one row per padded
+ * slot) and the per-pair down-projection outputs [T*top_k][H] fp32.  0 on bad
+ * arguments.
+ */
+size_t moe_gemm_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f);
+
+/*
+ * moe_expert_gemm -- the routed expert feed-forward of moe_expert_gemv at
+ * prompt batch (phobos-bench pp<N> through a mixture-of-experts layer): the
+ * same function of the same arguments,
+ *     y[t] = sum_s probs[t][s] * Wd[e] (silu(Wg[e] x_t) * (Wu[e] x_t)),
+ *     e = idx[t][s],  summed in slot order,
+ * computed as grouped products on the matrix cores: the (token, slot) pairs
+ * are grouped by expert and each selected expert's matrices are read once per
+ * 64 of its pairs.  x and h are rounded to bf16 and the weights decoded to bf16;
+ * products accumulate in fp32.  Each of the three products is within
+ * 8e-3 * sum |a w| of its exact value on its own (rounded) input, as for
+ * quant_gemm; use moe_expert_gemv for the tighter decode tolerance.  The result
+ * does not depend on the order in which pairs of one expert are processed, and
+ * repeated calls give identical results.
+ *   type, e, h, f, x, idx, probs, top_k, y   as for moe_expert_gemv
+ *          (T*top_k <= 65536; out-of-range idx entries count as expert 0 with
+ *          weight 0)
+ *   ws     device workspace >= moe_gemm_workspace_size(E, T, top_k, H, F) bytes,
+ *          256-byte aligned; its contents on entry do not matter
+ * T == 0 is a no-op.  Errors: GGQ_ERR_ARG (also when a bf16 copy of x or h
+ * would exceed 2 GiB), GGQ_ERR_ALIGN, GGQ_ERR_WORKSPACE, GGQ_ERR_UNSUPPORTED.
+ */
+int moe_expert_gemm(int type, const void *wg, const void *wu, const void *wd, int64_t e,
+                    int64_t h, int64_t f, const float *x, int64_t t, const int32_t *idx,
+                    const float *probs, int top_k, float *y, void *ws, size_t ws_bytes,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

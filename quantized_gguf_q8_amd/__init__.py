@@ -55,6 +55,9 @@ _SIGS = {
     "moe_workspace_h_offset": (_SZ, [_I64, _I64, _I]),
     "moe_expert_gemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _P, _P,
                              _SZ, _P]),
+    "moe_gemm_workspace_size": (_SZ, [_I64, _I64, _I, _I64, _I64]),
+    "moe_expert_gemm": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _P, _P,
+                             _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -318,6 +321,37 @@ def moe_expert_gemv(fmt: int, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tens
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _dev(ws, "ws", torch.uint8)
     _ck("moe_expert_gemv", _lib.moe_expert_gemv(fmt, _ptr(wg), _ptr(wu), _ptr(wd), e, h, f,
+                                                _ptr(x), t, _ptr(idx), _ptr(probs), top_k,
+                                                _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def moe_gemm_workspace_size(e: int, t: int, top_k: int, h: int, f: int) -> int:
+    return _lib.moe_gemm_workspace_size(e, t, top_k, h, f)
+
+
+def moe_expert_gemm(fmt: int, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor, e: int,
+                    h: int, f: int, x: torch.Tensor, idx: torch.Tensor, probs: torch.Tensor,
+                    y: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_expert_gemv's function at prompt batch, on the matrix cores (bf16
+    operands, fp32 accumulation; the prompt-GEMM tolerance).  Returns y [T, H]."""
+    _wbytes(wg, fmt, e * f, h, "wg")
+    _wbytes(wu, fmt, e * f, h, "wu")
+    _wbytes(wd, fmt, e * h, f, "wd")
+    _dev(x, "x", torch.float32)
+    _dev(idx, "idx", torch.int32)
+    _dev(probs, "probs", torch.float32)
+    t, top_k = idx.shape
+    if x.shape != (t, h) or probs.shape != (t, top_k):
+        raise ValueError("x, idx and probs disagree on T / H / top_k")
+    if y is None:
+        y = torch.empty((t, h), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    need = moe_gemm_workspace_size(e, t, top_k, h, f)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(ws, "ws", torch.uint8)
+    _ck("moe_expert_gemm", _lib.moe_expert_gemm(fmt, _ptr(wg), _ptr(wu), _ptr(wd), e, h, f,
                                                 _ptr(x), t, _ptr(idx), _ptr(probs), top_k,
                                                 _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y

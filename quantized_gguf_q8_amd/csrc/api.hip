@@ -231,10 +231,10 @@ size_t moe_workspace_h_offset(int64_t e, int64_t t, int top_k) {
     return ggq::moe_ws_h_offset(e, t, top_k);
 }
 
-int moe_expert_gemv(int type, const void* wg, const void* wu, const void* wd, int64_t e,
-                    int64_t h, int64_t f, const float* x, int64_t t, const int32_t* idx,
-                    const float* probs, int top_k, float* y, void* ws, size_t ws_bytes,
-                    void* stream) {
+// Arguments shared by the two expert feed-forward entry points.
+static int check_moe(int type, const void* wg, const void* wu, const void* wd, int64_t e, int64_t h,
+                     int64_t f, const float* x, int64_t t, const int32_t* idx, const float* probs,
+                     int top_k, float* y) {
     if (!block_of(type)) return GGQ_ERR_UNSUPPORTED;
     if (e < 1 || e > kMaxExperts || t < 0 || top_k < 1 || top_k > kMaxTopK || top_k > e)
         return GGQ_ERR_ARG;
@@ -246,12 +246,49 @@ int moe_expert_gemv(int type, const void* wg, const void* wu, const void* wd, in
     if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(x, 16) ||
         !aligned(y, 4) || !aligned(idx, 4) || !aligned(probs, 4))
         return GGQ_ERR_ALIGN;
+    return GGQ_OK;
+}
+
+int moe_expert_gemv(int type, const void* wg, const void* wu, const void* wd, int64_t e,
+                    int64_t h, int64_t f, const float* x, int64_t t, const int32_t* idx,
+                    const float* probs, int top_k, float* y, void* ws, size_t ws_bytes,
+                    void* stream) {
+    const int rc = check_moe(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y);
+    if (rc != GGQ_OK || t == 0) return rc;
     if (!ws || ws_bytes < ggq::moe_ws_bytes(e, t, top_k, h, f)) return GGQ_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
     return launched(ggq::launch_moe(type, static_cast<const uint8_t*>(wg),
                                     static_cast<const uint8_t*>(wu),
                                     static_cast<const uint8_t*>(wd), e, h, f, x, t, idx, probs,
                                     top_k, y, ws, as_stream(stream)));
+}
+
+size_t moe_gemm_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
+    if (e < 1 || e > kMaxExperts || t < 1 || top_k < 1 || top_k > kMaxTopK || h < 1 || f < 1)
+        return 0;
+    if (t * top_k > 65536) return 0;
+    return ggq::moe_gemm_ws_bytes(e, t, top_k, h, f);
+}
+
+int moe_expert_gemm(int type, const void* wg, const void* wu, const void* wd, int64_t e,
+                    int64_t h, int64_t f, const float* x, int64_t t, const int32_t* idx,
+                    const float* probs, int top_k, float* y, void* ws, size_t ws_bytes,
+                    void* stream) {
+    const int rc = check_moe(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y);
+    if (rc != GGQ_OK || t == 0) return rc;
+    // bf16 x and h are addressed with 31-bit buffer offsets, one expert's
+    // matrix with 32-bit ones
+    const int64_t slots = ggq::moe_gemm_slot_bound(e, t * top_k);
+    if (t * h * 2 >= ((int64_t)1 << 31) || slots * f * 2 >= ((int64_t)1 << 31)) return GGQ_ERR_ARG;
+    if (f * ggq::row_bytes(type, h) >= ((int64_t)1 << 32) ||
+        h * ggq::row_bytes(type, f) >= ((int64_t)1 << 32))
+        return GGQ_ERR_ARG;
+    if (!ws || ws_bytes < ggq::moe_gemm_ws_bytes(e, t, top_k, h, f)) return GGQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+    return launched(ggq::launch_moe_gemm(type, static_cast<const uint8_t*>(wg),
+                                         static_cast<const uint8_t*>(wu),
+                                         static_cast<const uint8_t*>(wd), e, h, f, x, t, idx,
+                                         probs, top_k, y, ws, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -165,8 +165,8 @@ __device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int k0,
         uint32_t lo[4], hi[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const uint32_t l = qw[i] & 0x0F0F0F0Fu;
-            const uint32_t h = (qw[i] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t l = opaque(qw[i] & 0x0F0F0F0Fu);
+            const uint32_t h = opaque((qw[i] >> 4) & 0x0F0F0F0Fu);
             lo[2 * i] = cvt_bf16x2(__builtin_fmaf(a0, ubyte_f(l, 0), b0), __builtin_fmaf(a0, ubyte_f(l, 1), b0));
             lo[2 * i + 1] = cvt_bf16x2(__builtin_fmaf(a0, ubyte_f(l, 2), b0), __builtin_fmaf(a0, ubyte_f(l, 3), b0));
             hi[2 * i] = cvt_bf16x2(__builtin_fmaf(a1, ubyte_f(h, 0), b1), __builtin_fmaf(a1, ubyte_f(h, 1), b1));

@@ -70,6 +70,15 @@ __device__ __forceinline__ float ubyte_f(uint32_t v, int i) {
     return static_cast<float>((v >> (8 * i)) & 0xFFu);
 }
 
+// The value unchanged, but opaque to the optimiser.  After a nibble mask
+// (q & 0x0F0F0F0F) the compiler otherwise uses the known zero bits to turn each
+// byte conversion into a bit-field extract plus v_cvt_f32_ubyte0, one more
+// instruction per weight than v_cvt_f32_ubyte{0,1,2,3} on the masked word.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs here are finite).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __builtin_bit_cast(uint32_t, f);

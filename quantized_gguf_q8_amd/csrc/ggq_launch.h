@@ -47,4 +47,17 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
                       const int32_t* idx, const float* probs, int top_k, float* y, void* ws,
                       hipStream_t s);
 
+// y[t] = sum_s probs[t][s] * dbuf[t*top_k + s] (slot order; out-of-range experts count 0).
+hipError_t launch_combine(const float* dbuf, const int32_t* idx, const float* probs, int64_t e,
+                          int64_t h, int64_t t, int top_k, float* y, hipStream_t s);
+
+// Routed expert feed-forward at prompt batch (grouped matrix-core GEMMs).
+int64_t moe_gemm_slot_bound(int64_t e, int64_t p);
+int64_t moe_gemm_tile_bound(int64_t e, int64_t p);
+size_t moe_gemm_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f);
+hipError_t launch_moe_gemm(int type, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
+                           int64_t e, int64_t h, int64_t f, const float* x, int64_t t,
+                           const int32_t* idx, const float* probs, int top_k, float* y, void* ws,
+                           hipStream_t s);
+
 }  // namespace ggq

@@ -1208,6 +1208,13 @@ hipError_t launch_swiglu(int type, const uint8_t* wg, const uint8_t* wu, int64_t
     return q4 ? launch_mstage<kQ4_K, 2>(a, 1, s) : launch_mstage<kQ8_0, 2>(a, 1, s);
 }
 
+hipError_t launch_combine(const float* dbuf, const int32_t* idx, const float* probs, int64_t e,
+                          int64_t h, int64_t t, int top_k, float* y, hipStream_t s) {
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((h + 255) / 256), (unsigned)t), dim3(256), 0,
+                       s, dbuf, idx, probs, e, h, top_k, y);
+    return hipGetLastError();
+}
+
 size_t moe_ws_h_offset(int64_t e, int64_t t, int top_k) { return ints_bytes(e, t * top_k); }
 
 size_t moe_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
@@ -1236,9 +1243,7 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
     else err = q4 ? launch_experts_mfma<kQ4_K>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
                   : launch_experts_mfma<kQ8_0>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((h + 255) / 256), (unsigned)t), dim3(256), 0,
-                       s, m.dbuf, idx, probs, e, h, top_k, y);
-    return hipGetLastError();
+    return launch_combine(m.dbuf, idx, probs, e, h, t, top_k, y, s);
 }
 
 }  // namespace ggq

@@ -40,3 +40,30 @@ def check_bound(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str) 
 
 def check_rel(got, ref, s, tol, what) -> float:
     return check_bound(got, ref, tol * np.asarray(s, dtype=np.float64), what)
+
+
+def moe_bound(fmt, mo, idx, probs, h, f, tol, tokens=None):
+    """Per-element bound on the routed expert layer when each of its three
+    products is within tol * sum|a w| of the exact product of its (rounded)
+    input: g and u errors dg, du propagate through h = silu(g) * u (|silu'| <=
+    1.1) as dh = 1.1|u|dg + |silu(g)|du + 1.1 dg du; the down product then adds
+    sum|wd|dh and tol * sum|wd|(|h| + dh); the fp32 activation and the combine
+    add 1e-6 of sum|wd h|.  Rows of `tokens` (default: all), in that order."""
+    import oracle
+
+    tokens = range(idx.shape[0]) if tokens is None else tokens
+    bound = np.zeros((len(tokens), h))
+    for i, ti in enumerate(tokens):
+        for s in range(idx.shape[1]):
+            ex = int(idx[ti, s])
+            if not 0 <= ex < mo["wg"].shape[0]:
+                continue
+            o = oracle.expert_ffn(fmt, mo["wg"], mo["wu"], mo["wd"], ex, h, f, mo["x"][ti])
+            sig = 1.0 / (1.0 + np.exp(-o["g"]))
+            dg = tol * o["sg"]
+            du = tol * o["su"]
+            dh = (1.1 * np.abs(o["u"]) * dg + np.abs(o["g"] * sig) * du + 1.1 * dg * du
+                  + 1e-6 * np.abs(o["h"]))
+            wabs, _ = oracle.matvec_f64(fmt, mo["wd"][ex], h, f, dh, absw=True)
+            bound[i] += float(probs[ti, s]) * (tol * o["sy"] + (1 + tol) * wabs + 1e-6 * o["sy"])
+    return bound

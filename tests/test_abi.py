@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     for n in ("quant_gemv", "quant_gemm", "moe_expert_gemv", "moe_route", "quant_dequantize",
               "quant_gemm_workspace_size", "moe_workspace_size", "moe_workspace_h_offset",
               "quant_gemv_workspace_size", "quant_gemv_split_workspace_size",
-              "quant_gemv_swiglu",
+              "quant_gemv_swiglu", "moe_expert_gemm", "moe_gemm_workspace_size",
               "ggq_status_string", "ggq_version"):
         assert n in names
 
@@ -199,3 +199,33 @@ def test_moe_validation(g):
     assert call(x=B16 + 8) == ALIGN
     assert call(wsb=need - 1) == WS
     assert call(ws=D16 + 64) == ALIGN
+
+
+def test_moe_gemm_validation(g):
+    L = g._lib
+    need = L.moe_gemm_workspace_size(128, 512, 8, 2048, 768)
+    p = 512 * 8
+    slots = p + 15 * 128
+    # bf16 x, bf16 h per padded slot, fp32 down outputs per pair, slot list
+    assert need >= 512 * 2048 * 2 + slots * 768 * 2 + p * 2048 * 4 + slots * 4
+    assert need < 512 * 2048 * 2 + slots * 768 * 2 + p * 2048 * 4 + slots * 4 + 64 * 1024
+    assert L.moe_gemm_workspace_size(0, 512, 8, 2048, 768) == 0
+    assert L.moe_gemm_workspace_size(128, 65537, 1, 2048, 768) == 0
+
+    def call(t=12, e=128, h=2048, f=768, tt=512, k=8, ws=D16, wsb=need, x=B16):
+        return L.moe_expert_gemm(t, A16, A16, A16, e, h, f, x, tt, C16, C16, k, C16, ws, wsb, None)
+
+    # (only failing variants are called: a valid call would launch kernels on fake pointers)
+    assert call(t=5) == UNSUP
+    assert call(h=2000) == ARG
+    assert call(f=100) == ARG
+    assert call(k=9, e=8) == ARG
+    assert call(e=1025) == ARG
+    assert call(tt=8193) == ARG                       # more than 65536 pairs
+    assert call(tt=65536, k=1, h=16384) == ARG        # bf16 x past 2 GiB
+    assert call(x=None) == ARG
+    assert call(x=B16 + 8) == ALIGN
+    assert call(wsb=need - 1) == WS
+    assert call(ws=None) == WS
+    assert call(ws=D16 + 64) == ALIGN
+    assert call(tt=0, x=None, ws=None) == OK           # no tokens: nothing to do

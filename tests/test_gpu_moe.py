@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from _gpu import GEMV_TOL, check_bound, check_rel, dev, host, say
+from _gpu import GEMV_TOL, check_bound, check_rel, dev, host, moe_bound, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -95,21 +95,10 @@ def test_route_many_experts(g, e, k):
 
 
 def _moe_bound(fmt, mo, x, idx, probs, e, h, f):
-    """First-order bound for the end-to-end expert layer (see module doc of
-    oracle.moe): per-GEMV 1e-5 tolerances propagated through silu(g)*u."""
-    t, k = idx.shape
-    bound = np.zeros((t, h))
-    for ti in range(t):
-        for s in range(k):
-            ex = int(idx[ti, s])
-            o = oracle.expert_ffn(fmt, mo["wg"], mo["wu"], mo["wd"], ex, h, f, x[ti])
-            sig = 1.0 / (1.0 + np.exp(-o["g"]))
-            dg = GEMV_TOL * o["sg"]
-            du = GEMV_TOL * o["su"]
-            dh = 1.1 * np.abs(o["u"]) * dg + np.abs(o["g"] * sig) * du + 1e-6 * np.abs(o["h"])
-            wabs, _ = oracle.matvec_f64(fmt, mo["wd"][ex], h, f, dh, absw=True)
-            bound[ti] += float(probs[ti, s]) * (GEMV_TOL * o["sy"] + wabs + 1e-6 * o["sy"])
-    return bound
+    """First-order bound for the end-to-end expert layer: per-GEMV 1e-5
+    tolerances propagated through silu(g)*u (x is mo["x"])."""
+    assert x is mo["x"]
+    return moe_bound(fmt, mo, idx, probs, h, f, GEMV_TOL)
 
 
 def _run_moe(g, fmt, mo, idx, probs, e, h, f):
