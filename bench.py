@@ -46,7 +46,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (HBM counter calibration)")
-    p.add_argument("--only", choices=["q4k", "moe", "ffn", "gemm", "sweep"], default=None,
+    p.add_argument("--only", choices=["q4k", "moe", "moe_prompt", "ffn", "gemm", "sweep"],
+                   default=None,
                    help="run one secondary workload only (for profiling)")
     return p.parse_args()
 
@@ -346,6 +347,53 @@ def secondary(g, torch, synth, only=None):
                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del graphs, sets
         out["moe_q4k"] = res
+    if only in (None, "moe_prompt"):
+        # The same routed layer at prompt batch through moe_expert_gemm (grouped
+        # matrix-core products), against the decode path (moe_expert_gemv) on
+        # the same tokens.
+        res = {}
+        e, h, f, k = synth.MOE_EXPERTS, synth.MOE_HIDDEN, synth.MOE_FFN, synth.MOE_TOP_K
+        for t in (64, 512):
+            mo = synth.moe_layer(seed=0, n_tokens=t)
+            wr = torch.from_numpy(mo["wr"]).to(dev)
+            layer_bytes = mo["wg"].nbytes + mo["wu"].nbytes + mo["wd"].nbytes
+            copies = max(2, -(-ROTATE_BYTES // layer_bytes))
+            sets = [tuple(torch.from_numpy(mo[key]).to(dev) for key in ("wg", "wu", "wd"))
+                    for _ in range(copies)]
+            x = torch.from_numpy(mo["x"]).to(dev)
+            idx0, _, _ = g.moe_route(wr, x, k)
+            distinct = int(torch.unique(idx0).numel())
+            ws = torch.empty(max(g.moe_gemm_workspace_size(e, t, k, h, f),
+                                 g.moe_workspace_size(e, t, k, h, f)), dtype=torch.uint8,
+                             device=dev)
+            y = torch.empty((t, h), dtype=torch.float32, device=dev)
+            per_expert = mo["wg"][0].nbytes + mo["wu"][0].nbytes + mo["wd"][0].nbytes
+            alg = distinct * per_expert + mo["wr"].nbytes
+            flop = 2.0 * t * k * 3 * h * f
+
+            def layer(c, fn):
+                def run():
+                    wg_, wu_, wd_ = sets[c]
+                    ii, pp, _ = g.moe_route(wr, x, k)
+                    fn(g.Q4_K, wg_, wu_, wd_, e, h, f, x, ii, pp, y, ws)
+                return run
+
+            graphs = capture(torch, [lambda: [layer(c, g.moe_expert_gemm)() for c in range(copies)]])
+            ms = replay_ms(torch, graphs, 20, copies)
+            del graphs
+            graphs = capture(torch, [lambda: [layer(c, g.moe_expert_gemv)() for c in range(copies)]])
+            ms_gemv = replay_ms(torch, graphs, 3, copies)
+            del graphs
+            gbs = alg / (ms * 1e-3) / 1e9
+            tflops = flop / (ms * 1e-3) / 1e12
+            res[f"t{t}"] = {"us": round(ms * 1e3, 2), "distinct_experts": distinct,
+                            "alg_bytes": alg, "GB/s": round(gbs, 1),
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "TFLOP/s": round(tflops, 1),
+                            "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+                            "decode_path_us": round(ms_gemv * 1e3, 2)}
+            del sets
+        out["moe_q4k_prompt"] = res
     if only in (None, "ffn"):
         # Dense FFN gate/up of the ~1B layer set fused with SiLU*up
         # (quant_gemv_swiglu) against the same two products as one grouped GEMV

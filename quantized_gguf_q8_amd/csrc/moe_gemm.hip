@@ -29,13 +29,18 @@
 // The result is within the prompt-GEMM tolerance of each product (8e-3 of the
 // sum of |a w|), propagated through silu(g)*u.
 //
-// K order inside the 16x16x32 products.  The lanes 16q..16q+15 of a wave own
-// columns 64q .. 64q+63 of each 256-column chunk -- two whole Q8_0 blocks, or
-// one 64-weight group of a Q4_K super-block (the low and high nibbles of the
-// same 32 quant bytes).  Product s (0..7) of a chunk takes, in lane group q,
-// the 8 columns 64q + 8s .. 64q + 8s + 7.  Any assignment of columns to
-// product slots gives the same sum as long as both operands use it; this one
-// lets a lane decode weights from the bytes it loaded itself.
+// K order inside the 16x16x32 products.  Any assignment of a chunk's 256
+// columns to (lane group q = lane / 16, product s, slot i) gives the same sums
+// as long as both operands use it; the one here lets each lane decode weights
+// from bytes it loaded itself, with the four lanes of a weight row reading
+// neighbouring bytes (mg_kcol):
+//   Q8_0: lanes of group q own blocks 2q and 2q+1 (columns 64q .. 64q+63);
+//         product s takes columns 64q + 8s .. +7.
+//   Q4_K: lanes of group q own quant bytes 16q .. 16q+15 and 64+16q .. +15 of
+//         the super-block, i.e. 16 low- and 16 high-nibble weights in each of
+//         the 64-weight groups q/2 and 2 + q/2; product s takes, in group
+//         q/2 + 2(s/4), the nibbles (low for s%4 < 2, high after) of bytes
+//         16(q%2) + 8(s%2) .. +7.
 #include <type_traits>
 
 #include "ggq_device.h"
@@ -225,10 +230,10 @@ __device__ __forceinline__ void mg_load(__amdgpu_buffer_rsrc_t r, uint32_t rowof
                                         MgRaw<FMT>& o) {
     if constexpr (FMT == kQ4_K) {
         const uint32_t b = rowoff == kOob ? kOob : rowoff + (uint32_t)c * kQ4Bytes;
-        const uint32_t bq = rowoff == kOob ? kOob : b + 16 + 32 * q;
+        const uint32_t bq = rowoff == kOob ? kOob : b + 16 + 16 * q;
         o.hdr = __builtin_amdgcn_raw_buffer_load_b128(r, b, 0, 0);
         o.q0 = __builtin_amdgcn_raw_buffer_load_b128(r, bq, 0, 0);
-        o.q1 = __builtin_amdgcn_raw_buffer_load_b128(r, rowoff == kOob ? kOob : bq + 16, 0, 0);
+        o.q1 = __builtin_amdgcn_raw_buffer_load_b128(r, rowoff == kOob ? kOob : bq + 64, 0, 0);
     } else {
         // dword aligned: rows and chunks start on 16 bytes, 68q on 4
         const uint32_t b = rowoff == kOob ? kOob : rowoff + (uint32_t)c * (8 * kQ8Bytes) + 68 * q;
@@ -240,10 +245,17 @@ __device__ __forceinline__ void mg_load(__amdgpu_buffer_rsrc_t r, uint32_t rowof
     }
 }
 
-// Per-chunk constants of a lane's weights: Q4_K the scale and offset of its
-// two sub-blocks (w = a*q + b); Q8_0 the two block scales.
+// First of the 8 columns (within a chunk) of product s in lane group q.
+template <int FMT>
+__host__ __device__ constexpr int mg_kcol(int q, int s) {
+    return FMT == kQ4_K ? 64 * (q / 2 + 2 * (s >> 2)) + 32 * ((s >> 1) & 1) + 16 * (q & 1) + 8 * (s & 1)
+                        : 64 * q + 8 * s;
+}
+
+// Per-chunk constants of a lane's weights (w = a*q + b): Q4_K its four
+// sub-blocks 2(q/2), +1, +4, +5; Q8_0 its two blocks (q + 128 read unsigned).
 struct MgScale {
-    float a0, b0, a1, b1;
+    float a[4], b[4];
 };
 
 template <int FMT>
@@ -253,19 +265,24 @@ __device__ __forceinline__ MgScale mg_scales(const MgRaw<FMT>& r, int q) {
         const float d = half_bits_to_float(r.hdr.x);
         const float dmin = half_bits_to_float(r.hdr.x >> 16);
         const Q4KScales sc = q4k_unpack(r.hdr.y, r.hdr.z, r.hdr.w);
-        uint32_t sc0, m0, sc1, m1;
-        q4k_sub(sc, 2 * q, sc0, m0);
-        q4k_sub(sc, 2 * q + 1, sc1, m1);
-        s.a0 = d * (float)sc0;
-        s.b0 = -dmin * (float)m0;
-        s.a1 = d * (float)sc1;
-        s.b1 = -dmin * (float)m1;
+        const int j0 = 2 * (q >> 1);
+        // sub-blocks j0, j0+1 < 4 read the low fields, j0+4, j0+5 the high ones
+        const uint32_t sc_[4] = {byte_of(sc.scl, j0), byte_of(sc.scl, j0 + 1), byte_of(sc.sch, j0),
+                                 byte_of(sc.sch, j0 + 1)};
+        const uint32_t m_[4] = {byte_of(sc.mnl, j0), byte_of(sc.mnl, j0 + 1), byte_of(sc.mnh, j0),
+                                byte_of(sc.mnh, j0 + 1)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s.a[i] = d * (float)sc_[i];
+            s.b[i] = -dmin * (float)m_[i];
+        }
     } else {
         (void)q;
-        s.a0 = half_bits_to_float(r.v0.x);
-        s.b0 = -128.f * s.a0;
-        s.a1 = half_bits_to_float(r.v2.x >> 16);   // bytes 34-35
-        s.b1 = -128.f * s.a1;
+        s.a[0] = half_bits_to_float(r.v0.x);
+        s.b[0] = -128.f * s.a[0];
+        s.a[1] = half_bits_to_float(r.v2.x >> 16);   // bytes 34-35
+        s.b[1] = -128.f * s.a[1];
+        s.a[2] = s.a[3] = s.b[2] = s.b[3] = 0.f;
     }
     return s;
 }
@@ -280,21 +297,21 @@ __device__ __forceinline__ bf16x8 mg_decode(const MgRaw<FMT>& r, const MgScale& 
     uint32_t w0, w1;
     float a, b;
     if constexpr (FMT == kQ4_K) {
-        // quant bytes 8(S%4) .. +7 of the group: low nibbles for S < 4, high after
-        constexpr int j = 2 * (S & 3);
-        const u32x4& src = j < 4 ? r.q0 : r.q1;
-        const uint32_t x0 = u4_at(src, j & 3), x1 = u4_at(src, (j & 3) + 1);
-        if constexpr (S < 4) {
+        // bytes 8(S%2) .. +7 of the lane's first (S < 4) or second 16 quant
+        // bytes; low nibbles for S%4 < 2, high after
+        const u32x4& src = S < 4 ? r.q0 : r.q1;
+        const uint32_t x0 = u4_at(src, 2 * (S & 1)), x1 = u4_at(src, 2 * (S & 1) + 1);
+        constexpr int hi = (S >> 1) & 1;
+        constexpr int sb = 2 * (S >> 2) + hi;
+        if constexpr (!hi) {
             w0 = opaque(x0 & 0x0F0F0F0Fu);
             w1 = opaque(x1 & 0x0F0F0F0Fu);
-            a = sc.a0;
-            b = sc.b0;
         } else {
             w0 = opaque((x0 >> 4) & 0x0F0F0F0Fu);
             w1 = opaque((x1 >> 4) & 0x0F0F0F0Fu);
-            a = sc.a1;
-            b = sc.b1;
         }
+        a = sc.a[sb];
+        b = sc.b[sb];
     } else {
         // bytes of the lane's 68: block 2q quants at 2..33, block 2q+1 at 36..67.
         // (q ^ 0x80) read as an unsigned byte is q + 128; a*(q+128) - 128a = a*q
@@ -305,13 +322,13 @@ __device__ __forceinline__ bf16x8 mg_decode(const MgRaw<FMT>& r, const MgScale& 
         if constexpr (S < 4) {
             w0 = __builtin_amdgcn_alignbyte(d[2 * S + 1], d[2 * S], 2);
             w1 = __builtin_amdgcn_alignbyte(d[2 * S + 2], d[2 * S + 1], 2);
-            a = sc.a0;
-            b = sc.b0;
+            a = sc.a[0];
+            b = sc.b[0];
         } else {
             w0 = d[9 + 2 * (S - 4)];
             w1 = d[10 + 2 * (S - 4)];
-            a = sc.a1;
-            b = sc.b1;
+            a = sc.a[1];
+            b = sc.b[1];
         }
         w0 ^= 0x80808080u;
         w1 ^= 0x80808080u;
@@ -356,39 +373,37 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
         roff[j] = col[j] < p.n ? (uint32_t)(col[j] * p.rb) : kOob;
     }
 
-    // activation staging: thread pieces i = 0..7 are row tid/32 + 8i, piece
+    // activation staging: thread pieces i = 0..2G-1 are row tid/32 + 8i, piece
     // u = tid % 32 (product u % 8, lane group u / 8) of that row's chunk
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.abytes);
     const int u = tid & 31, us = u & 7, uq = u >> 3;
-    uint32_t asrc[8];
-    int adst[8];
+    const uint32_t acol = (uint32_t)(2 * mg_kcol<FMT>(uq, us));
+    uint32_t asrc[2 * G];   // byte offset of the row's first chunk, or kOob
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = (tid >> 5) + 8 * i;
-        asrc[i] = kOob;
-        if (r < 16 * G) {
-            const int slot = row0 + r;
-            int src = slot;
-            if (p.adiv > 0) {
-                const int pr = p.spair[slot];
-                src = pr >= 0 ? pr / p.adiv : -1;
-            }
-            if (src >= 0) asrc[i] = (uint32_t)src * (uint32_t)p.k * 2u + (uint32_t)(128 * uq + 16 * us);
+    for (int i = 0; i < 2 * G; ++i) {
+        const int slot = row0 + (tid >> 5) + 8 * i;
+        int src = slot;
+        if (p.adiv > 0) {
+            const int pr = p.spair[slot];
+            src = pr >= 0 ? pr / p.adiv : -1;
         }
-        adst[i] = mg_lds_off(us, r >> 4, (r & 15) + 16 * uq);
+        asrc[i] = src >= 0 ? (uint32_t)src * (uint32_t)p.k * 2u + acol : kOob;
     }
-    u32x4 av[8];
+    // LDS destination of piece i: row r = tid/32 + 8i has group i/2 and row
+    // (tid/32) + 8(i%2) within it, so the offsets differ by constants
+    const int adst0 = mg_lds_off(us, 0, (tid >> 5) + 16 * uq);
+    u32x4 av[2 * G];
     auto load_a = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < 2 * G)
-                av[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    ra, asrc[i] == kOob ? kOob : asrc[i] + (uint32_t)c * (kKC * 2), 0, 0);
+        for (int i = 0; i < 2 * G; ++i) {
+            const uint32_t off = asrc[i] == kOob ? kOob : asrc[i] + (uint32_t)c * (kKC * 2);
+            av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+        }
     };
     auto store_a = [&](uint8_t* buf) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < 2 * G) *reinterpret_cast<u32x4*>(buf + adst[i]) = av[i];
+        for (int i = 0; i < 2 * G; ++i)
+            *reinterpret_cast<u32x4*>(buf + adst0 + (i >> 1) * kAFrag + (i & 1) * 128) = av[i];
     };
 
     MgRaw<FMT> rw[2][NT];
@@ -441,25 +456,33 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     // Weights and activations run one chunk ahead (two register sets for the
     // weights, named statically: two chunks per trip; two LDS buffers for the
     // activations).  A chunk's activation loads are issued before its weight
-    // loads, so storing them to LDS does not wait for the weights.
+    // loads, so storing them to LDS does not wait for the weights.  Inside the
+    // loop every chunk has a successor and its loads are unconditional: a
+    // branch around them would leave the wait counter unknown at the join, and
+    // the compiler would then wait for the prefetch before using the current
+    // chunk.  The last chunk (no successor) is peeled off.
     const int nc = p.k / kKC;
     load_a(0);
     load_w(0, rw[0]);
     store_a(lds);
     __syncthreads();
-    auto body = [&](int c, const MgRaw<FMT> (&cur)[NT], MgRaw<FMT> (&nxt)[NT]) {
-        if (c + 1 < nc) {
-            load_a(c + 1);
-            load_w(c + 1, nxt);
-        }
+    auto step = [&](int c, const MgRaw<FMT> (&cur)[NT], MgRaw<FMT> (&nxt)[NT]) {
+        load_a(c + 1);
+        load_w(c + 1, nxt);
         compute(lds + (c & 1) * kABuf, cur);
-        if (c + 1 < nc) store_a(lds + ((c + 1) & 1) * kABuf);
+        store_a(lds + ((c + 1) & 1) * kABuf);
         __syncthreads();
     };
-    for (int c = 0; c < nc; c += 2) {
-        body(c, rw[0], rw[1]);
-        if (c + 1 >= nc) break;
-        body(c + 1, rw[1], rw[0]);
+    int c = 0;
+    for (; c + 2 < nc; c += 2) {
+        step(c, rw[0], rw[1]);
+        step(c + 1, rw[1], rw[0]);
+    }
+    if (c + 1 < nc) {
+        step(c, rw[0], rw[1]);
+        compute(lds + ((c + 1) & 1) * kABuf, rw[1]);
+    } else {
+        compute(lds + (c & 1) * kABuf, rw[0]);
     }
 
     // D layout: lane holds rows 4*(lane/16) + r, column lane % 16 of each product
