@@ -37,11 +37,16 @@ def _run(cmd):
     return err
 
 
-# Per-source flags.  The decode GEMV and expert kernels keep MFMA results in
-# ordinary VGPRs: their few accumulators are rescaled by the vector units after
-# every block, and with AGPR results each rescale first needed a v_accvgpr_read.
+# Per-source flags.  The decode GEMV keeps MFMA results in ordinary VGPRs: its
+# few accumulators are rescaled by the vector units after every block, and with
+# AGPR results each rescale first needed a v_accvgpr_read.  It also asks a work
+# counter with one atomic from one lane while the next unit's loads are in
+# flight; the atomic optimiser rewrites that atomic into a wave-wide form whose
+# result is read back at once, and since the load counter drains in order that
+# read waited for the whole prefetch before the current unit's compute.
 FILE_FLAGS = {
-    "gemv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
+                      "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }
 
 

@@ -246,6 +246,10 @@ static int check_moe(int type, const void* wg, const void* wu, const void* wd, i
     if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) || !aligned(x, 16) ||
         !aligned(y, 4) || !aligned(idx, 4) || !aligned(probs, 4))
         return GGQ_ERR_ALIGN;
+    // one expert's matrix is addressed with 32-bit buffer offsets
+    if (f * ggq::row_bytes(type, h) >= ((int64_t)1 << 32) ||
+        h * ggq::row_bytes(type, f) >= ((int64_t)1 << 32))
+        return GGQ_ERR_ARG;
     return GGQ_OK;
 }
 
@@ -276,13 +280,9 @@ int moe_expert_gemm(int type, const void* wg, const void* wu, const void* wd, in
                     void* stream) {
     const int rc = check_moe(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y);
     if (rc != GGQ_OK || t == 0) return rc;
-    // bf16 x and h are addressed with 31-bit buffer offsets, one expert's
-    // matrix with 32-bit ones
+    // bf16 x and h are addressed with 31-bit buffer offsets
     const int64_t slots = ggq::moe_gemm_slot_bound(e, t * top_k);
     if (t * h * 2 >= ((int64_t)1 << 31) || slots * f * 2 >= ((int64_t)1 << 31)) return GGQ_ERR_ARG;
-    if (f * ggq::row_bytes(type, h) >= ((int64_t)1 << 32) ||
-        h * ggq::row_bytes(type, f) >= ((int64_t)1 << 32))
-        return GGQ_ERR_ARG;
     if (!ws || ws_bytes < ggq::moe_gemm_ws_bytes(e, t, top_k, h, f)) return GGQ_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
     return launched(ggq::launch_moe_gemm(type, static_cast<const uint8_t*>(wg),

@@ -50,6 +50,11 @@ struct MPos {
 // odd chunk.
 template <int RWG>
 __device__ __forceinline__ MPos mlocate(const MJobs& jobs, int item) {
+    // The item is the same for the whole workgroup (it may come through LDS,
+    // where the compiler cannot see that): with it in a scalar register the
+    // job fields are scalar loads and the buffer descriptors built from them
+    // stay scalar (a per-lane descriptor becomes a loop over lanes).
+    item = __builtin_amdgcn_readfirstlane(item);
     int j = 0;
     while (j + 1 < jobs.count && item >= jobs.j[j + 1].item0) ++j;
     const MJob& jb = jobs.j[j];
@@ -141,7 +146,7 @@ struct MPrefetch {
         const uint32_t rb = p.rb;
         const uint32_t cb0 = (uint32_t)p.chunk * C::CRB;
         const uint32_t base = (uint32_t)p.r0 * rb + cb0;
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + base, (uint32_t)p.n * rb - base);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc_uniform(p.w + base, (uint32_t)p.n * rb - base);
 #pragma unroll
         for (int i = 0; i < C::WP; ++i) {
             uint32_t src = wrel[i];
@@ -149,7 +154,8 @@ struct MPrefetch {
             if constexpr (FMT == kQ4_K) src = cb0 + woff[i] < rb ? src : kOob;
             w[i] = buf_load16<false>(rw, src);
         }
-        const __amdgpu_buffer_rsrc_t rf = make_rsrc(jb.xf, (uint32_t)xf_layout(FMT, jb.k, MT).bytes);
+        const __amdgpu_buffer_rsrc_t rf =
+            make_rsrc_uniform(jb.xf, (uint32_t)xf_layout(FMT, jb.k, MT).bytes);
 #pragma unroll
         for (int i = 0; i < C::FP; ++i) {
             uint32_t src;
@@ -274,7 +280,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const MJobs jobs, int ba
     if (ask && tid == 0) s_item[0] = g + atomicAdd(jobs.ctr, 1);
     pf.store(lds, tid);
     __syncthreads();
-    int qnext = ask ? s_item[0] : 0;   // next item; known once cur is its item's last unit
+    // next item; known once cur is its item's last unit (uniform: see mlocate)
+    int qnext = ask ? __builtin_amdgcn_readfirstlane(s_item[0]) : 0;
     int qslot = 1;
 
     f32x4 acc[MT];
@@ -296,9 +303,13 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const MJobs jobs, int ba
             more = false;
         }
         ask = more && nxt.chunk + 1 == nxt.cend;
-        if (more) pf.load(jobs, nxt, tid);
-        int got = 0;
+        // The counter is asked before the loads and its answer read after the
+        // compute: loads complete in issue order as far as the wait counter
+        // is concerned, so reading an answer issued after them would first
+        // wait for the whole prefetch.  (`got` is only defined where read.)
+        int got;
         if (ask && tid == 0) got = atomicAdd(jobs.ctr, 1);
+        if (more) pf.load(jobs, nxt, tid);
         mfma_unit<FMT, MT, WM>(jobs, cur, lds + buf * C::kBuf, lds + 2 * C::kBuf, batch, lane, wm, wk,
                                j, h, acc);
         if (!more) break;
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(const MJobs jobs, int ba
         pf.store(lds + buf * C::kBuf, tid);
         __syncthreads();
         if (ask) {
-            qnext = s_item[qslot];
+            qnext = __builtin_amdgcn_readfirstlane(s_item[qslot]);
             qslot ^= 1;
         }
         cur = nxt;

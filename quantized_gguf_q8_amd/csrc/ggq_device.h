@@ -107,6 +107,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              0x00020000);
 }
 
+// The same for a base and size that are equal across the wave but that the
+// compiler cannot prove so (values carried through loops and LDS): it takes
+// lane 0's, so the descriptor sits in scalar registers.  A descriptor in
+// vector registers makes every load through it a loop over distinct lanes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base,
+                                                                    uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                     __builtin_amdgcn_readfirstlane(bytes));
+}
+
 constexpr uint32_t kOob = 0xFFFFFFF0u;  // an offset past any descriptor's range
 
 // 16-byte buffer load; `nt` marks data read exactly once (non-temporal).

@@ -328,6 +328,16 @@ struct MoeLists {
 
 constexpr int kInlinePairs = 256;   // up to this many pairs are grouped in LDS
 
+// Element i of a pair list that lives in LDS (LDSL) or in the workspace.  The
+// address space is fixed at compile time: read through a generic pointer, an
+// LDS list entry is a flat load, which the hardware counts with the global
+// loads, so waiting for it would also wait for every weight load issued before.
+template <bool LDSL>
+__device__ __forceinline__ int32_t lget(const int32_t* p, int i) {
+    if constexpr (LDSL) return ((const __attribute__((address_space(3))) int32_t*)p)[i];
+    else return ((const __attribute__((address_space(1))) int32_t*)p)[i];
+}
+
 __host__ __device__ inline int inline_group_bytes(int64_t e, int64_t p) {
     return (int)((3 * e + 1 + 3 * p) * 4);
 }
@@ -446,22 +456,23 @@ struct MoeUnit {
     const int32_t* xrows;  // activation row per pair, or null: pair / xdiv
 };
 
-template <int ROWS>
+template <int ROWS, bool LDSL>
 __device__ __forceinline__ bool moe_locate(const MoeStage& st, const MoeLists& L, int tile,
                                            int total, MoeUnit& u) {
     if (tile >= total) return false;
     u.tile = tile;
-    u.e = L.active[tile / st.tiles];
+    u.e = lget<LDSL>(L.active, tile / st.tiles);
     u.r0 = (int64_t)(tile % st.tiles) * ROWS;
     u.g0 = 0;
-    u.cnt = L.cnt[u.e];
+    u.cnt = lget<LDSL>(L.cnt, u.e);
     u.chunk = 0;
-    u.pairs = L.list + L.off[u.e];
-    u.xrows = L.xrow ? L.xrow + L.off[u.e] : nullptr;
+    const int off = lget<LDSL>(L.off, u.e);
+    u.pairs = L.list + off;
+    u.xrows = L.xrow ? L.xrow + off : nullptr;
     return true;
 }
 
-template <int NB, int ROWS>
+template <int NB, int ROWS, bool LDSL>
 __device__ __forceinline__ bool moe_next(const MoeStage& st, const MoeLists& L, const MoeUnit& p,
                                          int total, MoeUnit& q) {
     q = p;
@@ -474,7 +485,7 @@ __device__ __forceinline__ bool moe_next(const MoeStage& st, const MoeLists& L, 
         q.chunk = 0;
         return true;
     }
-    return moe_locate<ROWS>(st, L, p.tile + (int)gridDim.x, total, q);
+    return moe_locate<ROWS, LDSL>(st, L, p.tile + (int)gridDim.x, total, q);
 }
 
 template <int FMT, int NB, int ROWS, int NMAT>
@@ -483,12 +494,16 @@ struct MoePrefetch {
     uint4 w[C::WP];
     uint4 x[C::XP];
 
+    // Every load is issued whether or not the unit is `live`; when it is not
+    // (no next unit) they read past their descriptors and touch no memory (a
+    // branch around them would make the compiler wait for them at the join).
     __device__ __forceinline__ void load_w(const MoeStage& st, const MoeUnit& u, int tid,
-                                           int wave) {
+                                           int wave, bool live) {
         const uint32_t bytes = (uint32_t)(st.n * st.rb);
-        const __amdgpu_buffer_rsrc_t r0 = make_rsrc(st.w[0] + (int64_t)u.e * st.n * st.rb, bytes);
+        const __amdgpu_buffer_rsrc_t r0 =
+            make_rsrc_uniform(st.w[0] + (int64_t)u.e * st.n * st.rb, bytes);
         const __amdgpu_buffer_rsrc_t r1 =
-            make_rsrc(st.w[NMAT - 1] + (int64_t)u.e * st.n * st.rb, bytes);
+            make_rsrc_uniform(st.w[NMAT - 1] + (int64_t)u.e * st.n * st.rb, bytes);
         const uint32_t cb0 = (uint32_t)u.chunk * C::CRB;
         const uint32_t rb = (uint32_t)st.rb;
 #pragma unroll
@@ -498,12 +513,14 @@ struct MoePrefetch {
             const int qm = q - m * C::MPIECES;
             const uint32_t row = (uint32_t)u.r0 + (uint32_t)(qm / C::PPR);
             const uint32_t off = (uint32_t)(qm % C::PPR) * 16;
-            const bool ok = q < C::WPIECES && row < (uint32_t)st.n && cb0 + off < rb;
+            const bool ok = live && q < C::WPIECES && row < (uint32_t)st.n && cb0 + off < rb;
             w[i] = buf_load16<true>(m ? r1 : r0, ok ? row * rb + cb0 + off : kOob);
         }
     }
 
-    __device__ __forceinline__ void load_x(const MoeStage& st, const MoeUnit& u, int tid) {
+    template <bool LDSL>
+    __device__ __forceinline__ void load_x(const MoeStage& st, const MoeUnit& u, int tid,
+                                           bool live) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(st.x, (uint32_t)(st.xrows * st.ldx * 4));
         const int k0 = u.chunk * C::KC;
         const int batch = min(NB, u.cnt - u.g0);
@@ -512,11 +529,10 @@ struct MoePrefetch {
             const int q = tid + 256 * i;
             const int b = q / (C::KC / 4);
             const int pos = (q % (C::KC / 4)) * 4;
-            if (b >= batch) continue;   // uniform per wave: a wave's pieces share b
             uint32_t off = kOob;
-            if (q < C::XPIECES && k0 + pos < st.k) {
-                const int64_t xr =
-                    u.xrows ? u.xrows[u.g0 + b] : u.pairs[u.g0 + b] / st.xdiv;
+            if (live && b < batch && q < C::XPIECES && k0 + pos < st.k) {
+                const int64_t xr = u.xrows ? lget<LDSL>(u.xrows, u.g0 + b)
+                                           : lget<LDSL>(u.pairs, u.g0 + b) / st.xdiv;
                 off = (uint32_t)((xr * st.ldx + k0 + pos) * 4);
             }
             x[i] = buf_load16<false>(r, off);
@@ -560,7 +576,7 @@ struct MoePrefetch {
     }
 };
 
-template <int FMT, int NB, int ROWS, int NMAT>
+template <int FMT, int NB, int ROWS, int NMAT, bool LDSL>
 __device__ __forceinline__ void moe_compute(const MoeStage& st, const MoeUnit& u,
                                             const uint8_t* lw, const uint8_t* xbuf, int s, int rl,
                                             float (&acc)[NMAT][NB]) {
@@ -615,7 +631,7 @@ __device__ __forceinline__ void moe_compute(const MoeStage& st, const MoeUnit& u
                         const float g = acc[0][b];
                         v = g / (1.0f + expf(-g)) * acc[1][b];
                     }
-                    st.y[(int64_t)u.pairs[u.g0 + b] * st.ldy + u.r0 + rl] = v;
+                    st.y[(int64_t)lget<LDSL>(u.pairs, u.g0 + b) * st.ldy + u.r0 + rl] = v;
                 }
             }
         }
@@ -628,7 +644,7 @@ __device__ __forceinline__ void moe_compute(const MoeStage& st, const MoeUnit& u
 
 // SINGLE: launched so that every workgroup computes one unit; LDS then holds
 // one W and one x buffer instead of two of each (pair lists follow them).
-template <int FMT, int NB, int ROWS, int NMAT, bool SINGLE>
+template <int FMT, int NB, int ROWS, int NMAT, bool SINGLE, bool LDSL>
 __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
     using C = MoeCfg<FMT, NB, ROWS, NMAT>;
     extern __shared__ __align__(16) uint8_t lds[];
@@ -639,7 +655,7 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
     const int s = tid % C::SL;
     const int rl = tid / C::SL;
     MoeLists L;
-    if (st.inline_group) {
+    if constexpr (LDSL) {
         uint8_t* lists = SINGLE ? lds + C::kWBytes + C::kXBuf : lds + C::kLds;
         L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lists));
     } else {
@@ -648,10 +664,10 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
     const int total = L.nact * st.tiles;
 
     MoeUnit cur;
-    if (!moe_locate<ROWS>(st, L, blockIdx.x, total, cur)) return;
+    if (!moe_locate<ROWS, LDSL>(st, L, blockIdx.x, total, cur)) return;
     MoePrefetch<FMT, NB, ROWS, NMAT> pf;
-    pf.load_w(st, cur, tid, wave);
-    pf.load_x(st, cur, tid);
+    pf.load_w(st, cur, tid, wave, true);
+    pf.template load_x<LDSL>(st, cur, tid, true);
     pf.store_w(lw0, tid);
     pf.store_x(lx0, tid, min(NB, cur.cnt - cur.g0));
     __syncthreads();
@@ -665,13 +681,22 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
     int buf = 0;
     for (;;) {
         MoeUnit nxt;
-        const bool more = moe_next<NB, ROWS>(st, L, cur, total, nxt);
-        if (more) {
-            pf.load_w(st, nxt, tid, wave);
-            pf.load_x(st, nxt, tid);
+        const bool more = moe_next<NB, ROWS, LDSL>(st, L, cur, total, nxt);
+        if constexpr (SINGLE) {
+            // normally one unit per workgroup: nothing to prefetch
+            if (more) {
+                pf.load_w(st, nxt, tid, wave, true);
+                pf.template load_x<LDSL>(st, nxt, tid, true);
+            }
+        } else {
+            // unconditional (past the last unit they read nothing): a branch
+            // around the loads would make the compiler wait for them where the
+            // paths join, before this unit's compute
+            pf.load_w(st, more ? nxt : cur, tid, wave, more);
+            pf.template load_x<LDSL>(st, more ? nxt : cur, tid, more);
         }
-        moe_compute<FMT, NB, ROWS, NMAT>(st, cur, lw0 + buf * C::kWBytes, lx0 + buf * C::kXBuf, s,
-                                         rl, acc);
+        moe_compute<FMT, NB, ROWS, NMAT, LDSL>(st, cur, lw0 + buf * C::kWBytes,
+                                               lx0 + buf * C::kXBuf, s, rl, acc);
         if (!more) break;
         // With one buffer (more units than planned, e.g. an expert repeated in a
         // token's slots) wait until every wave is done with it.
@@ -713,7 +738,9 @@ struct MoeMCfg {
     using C = MCfg<FMT, 1, 4>;         // 64 B rows, chunk KC, fragments of 8 slots
     static constexpr int RPM = 64 / NMAT;                 // rows of each matrix per tile
     static constexpr int PPR = C::CRB / 16;                // 16-byte pieces per row chunk
-    static constexpr int WPIECES = 64 * PPR;
+    static constexpr int WMP = RPM * PPR;                  // weight pieces per matrix ...
+    static constexpr int WMPAD = (WMP + 63) / 64 * 64;     // ... padded to whole waves
+    static constexpr int WPIECES = NMAT * WMPAD;
     static constexpr int WP = (WPIECES + 255) / 256;
     static constexpr int FPIECES = C::kFrag / 16;          // 16-byte fragment pieces
     static constexpr int FP = (FPIECES + 255) / 256;
@@ -733,23 +760,31 @@ struct MoeMPrefetch {
     uint4 f[M::FP];
     uint2 mn[M::MP > 0 ? M::MP : 1];
     float inv;
+    int ibatch;     // slots of the unit (inv beyond them is stored as 1)
 
+    uint32_t wok;   // bit i: weight piece i lies inside the matrix (else stored as zeros)
+
+    // A select on a loaded value (zeroing a piece, a default) would wait for
+    // the load at once, so out-of-range pieces are zeroed when stored.
+    template <bool LDSL>
     __device__ __forceinline__ void load(const MoeMfma& st, const MoeUnit& u, int tid) {
         const int batch = min(8, u.cnt - u.g0);
         const uint32_t cb0 = (uint32_t)u.chunk * C::CRB;
-        // weights: B row br = m * RPM + rr; per-lane addresses (the matrix varies
-        // within a wave), clamped to a valid byte and zeroed when out of range
+        // weights: piece q of matrix m = q / WMPAD, row q % WMPAD / PPR of the
+        // tile; per-lane addresses, clamped to a valid byte
+        wok = 0;
 #pragma unroll
         for (int i = 0; i < M::WP; ++i) {
             const int q = tid + 256 * i;
-            const int br = q / M::PPR, off = (q % M::PPR) * 16;
-            const int m = br / M::RPM;
-            const int64_t r = u.r0 + br % M::RPM;
-            const bool ok = q < M::WPIECES && r < st.n && cb0 + off < st.rb;
+            const int m = q / M::WMPAD;
+            const int qm = q - m * M::WMPAD;
+            const int64_t r = u.r0 + qm / M::PPR;
+            const uint32_t off = (uint32_t)(qm % M::PPR) * 16;
+            const bool ok = m < NMAT && qm < M::WMP && r < st.n && cb0 + off < st.rb;
             const uint8_t* src = st.w[m < NMAT ? m : 0] + ((int64_t)u.e * st.n + (ok ? r : 0)) * st.rb +
                                  (ok ? cb0 + off : 0);
-            const uint4 v = load_once16(src);
-            w[i] = ok ? v : make_uint4(0, 0, 0, 0);
+            w[i] = load_once16(src);
+            wok |= (uint32_t)ok << i;
         }
         // activation fragments gathered per slot: lane l of block b holds slot
         // (l % 16) / 2, hi/lo l % 2, k-octet l / 16
@@ -764,7 +799,7 @@ struct MoeMPrefetch {
             uint32_t off = kOob;
             const int kb = u.chunk * C::NBLK + blk;
             if (q < M::FPIECES && sl < batch && kb < nblk) {
-                const int row = u.xrows ? u.xrows[u.g0 + sl] : u.pairs[u.g0 + sl] / st.xdiv;
+                const int row = u.xrows ? lget<LDSL>(u.xrows, u.g0 + sl) : lget<LDSL>(u.pairs, u.g0 + sl) / st.xdiv;
                 const int sln = 2 * (row & 7) + (l & 1) + 16 * (l >> 4);
                 off = (uint32_t)(L.frag + (((int64_t)(row >> 3) * nblk + kb) * 64 + sln) * 16);
             }
@@ -779,7 +814,7 @@ struct MoeMPrefetch {
                 const int ksb = u.chunk * C::NSB + sb;
                 uint32_t off = kOob;
                 if (q < M::MPIECES && sl < batch && (l >> 4) < 2 && ksb < nsb) {
-                    const int row = u.xrows ? u.xrows[u.g0 + sl] : u.pairs[u.g0 + sl] / st.xdiv;
+                    const int row = u.xrows ? lget<LDSL>(u.xrows, u.g0 + sl) : lget<LDSL>(u.pairs, u.g0 + sl) / st.xdiv;
                     const int sln = 2 * (row & 7) + (l & 1) + 16 * (l >> 4);
                     off = (uint32_t)(L.mins + (((int64_t)(row >> 3) * nsb + ksb) * 64 + sln) * 8);
                 }
@@ -788,10 +823,14 @@ struct MoeMPrefetch {
                 mn[i] = make_uint2(v.x, v.y);
             }
         }
-        inv = 1.f;
-        if (tid < batch) {
-            const int row = u.xrows ? u.xrows[u.g0 + tid] : u.pairs[u.g0 + tid] / st.xdiv;
-            inv = reinterpret_cast<const float*>(st.xf + L.inv)[row];
+        // 2^-S of each slot; slots past the group read slot 0's row and are
+        // set to 1 when stored
+        ibatch = batch;
+        if (tid < 8) {
+            const int t = tid < batch ? tid : 0;
+            const int row = u.xrows ? lget<LDSL>(u.xrows, u.g0 + t) : lget<LDSL>(u.pairs, u.g0 + t) / st.xdiv;
+            inv = __builtin_bit_cast(float,
+                                     __builtin_amdgcn_raw_buffer_load_b32(rf, (uint32_t)(L.inv + 4 * row), 0, 0));
         }
     }
 
@@ -799,8 +838,11 @@ struct MoeMPrefetch {
 #pragma unroll
         for (int i = 0; i < M::WP; ++i) {
             const int q = tid + 256 * i;
-            if (q < M::WPIECES)
-                *reinterpret_cast<uint4*>(buf + (q / M::PPR) * C::RS + (q % M::PPR) * 16) = w[i];
+            const int m = q / M::WMPAD, qm = q % M::WMPAD;
+            if (m < NMAT && qm < M::WMP)
+                *reinterpret_cast<uint4*>(buf + (m * M::RPM + qm / M::PPR) * C::RS +
+                                          (qm % M::PPR) * 16) =
+                    (wok >> i) & 1u ? w[i] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < M::FP; ++i) {
@@ -814,11 +856,11 @@ struct MoeMPrefetch {
                 if (q < M::MPIECES) *reinterpret_cast<uint2*>(buf + C::kW + C::kFrag + q * 8) = mn[i];
             }
         }
-        if (tid < 8) reinterpret_cast<float*>(buf + M::kInvOff)[tid] = inv;
+        if (tid < 8) reinterpret_cast<float*>(buf + M::kInvOff)[tid] = tid < ibatch ? inv : 1.f;
     }
 };
 
-template <int FMT, int NMAT>
+template <int FMT, int NMAT, bool LDSL>
 __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
     using M = MoeMCfg<FMT, NMAT>;
     using C = typename M::C;
@@ -830,7 +872,7 @@ __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
     const int h = lane >> 4;   // D rows 4h .. 4h+3 = slots 2h, 2h+1 (hi, lo)
 
     MoeLists L;
-    if (st.inline_group) {
+    if constexpr (LDSL) {
         L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lds + M::kLds));
     } else {
         L = MoeLists{st.ws.cnt, st.ws.off, st.ws.active, st.ws.list, nullptr, st.ws.nact[0]};
@@ -841,9 +883,9 @@ __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
     ms.nchunk = st.nchunk;
     ms.tiles = st.tiles;
     MoeUnit cur;
-    if (!moe_locate<M::RPM>(ms, L, blockIdx.x, total, cur)) return;
+    if (!moe_locate<M::RPM, LDSL>(ms, L, blockIdx.x, total, cur)) return;
     MoeMPrefetch<FMT, NMAT> pf;
-    pf.load(st, cur, tid);
+    pf.template load<LDSL>(st, cur, tid);
     pf.store(lds, tid);
     __syncthreads();
 
@@ -851,8 +893,11 @@ __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
     int buf = 0;
     for (;;) {
         MoeUnit nxt;
-        const bool more = moe_next<8, M::RPM>(ms, L, cur, total, nxt);
-        if (more) pf.load(st, nxt, tid);
+        const bool more = moe_next<8, M::RPM, LDSL>(ms, L, cur, total, nxt);
+        // unconditional (the last unit reloads itself, from L2, unused): a
+        // branch around the loads would make the compiler wait for them where
+        // the paths join, before this unit's compute
+        pf.template load<LDSL>(st, more ? nxt : cur, tid);
         const uint8_t* base = lds + buf * M::kBuf;
         mfma_chunk<FMT, 1, 4>(base, cur.chunk * C::KC, st.k, lane, wave, 0, j, h, acc);
         if (cur.chunk == st.nchunk - 1) {
@@ -873,15 +918,15 @@ __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
                 if (wave < 2 && r < st.n) {
                     const float u0 = red[(wave * 64 + lane) * 2], u1 = red[(wave * 64 + lane) * 2 + 1];
                     if (2 * h < batch)
-                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.ldy + r] = v0 / (1.0f + expf(-v0)) * u0;
+                        st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h) * st.ldy + r] = v0 / (1.0f + expf(-v0)) * u0;
                     if (2 * h + 1 < batch)
-                        st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.ldy + r] = v1 / (1.0f + expf(-v1)) * u1;
+                        st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h + 1) * st.ldy + r] = v1 / (1.0f + expf(-v1)) * u1;
                 }
                 __syncthreads();
             } else {
                 if (r < st.n) {
-                    if (2 * h < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h] * st.ldy + r] = v0;
-                    if (2 * h + 1 < batch) st.y[(int64_t)cur.pairs[cur.g0 + 2 * h + 1] * st.ldy + r] = v1;
+                    if (2 * h < batch) st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h) * st.ldy + r] = v0;
+                    if (2 * h + 1 < batch) st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h + 1) * st.ldy + r] = v1;
                 }
             }
             acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -928,15 +973,16 @@ int moe_device_cus() {
 
 // Resident workgroups per compute unit of a stage kernel at an LDS size (the
 // last two sizes asked are cached).
-template <int FMT, int NB, int ROWS, int NMAT, bool SINGLE>
+template <int FMT, int NB, int ROWS, int NMAT, bool SINGLE, bool LDSL>
 int stage_blocks_per_cu(size_t lds) {
     static size_t key[2] = {0, 0};
     static int val[2] = {0, 0};
     for (int i = 0; i < 2; ++i)
         if (key[i] == lds) return val[i];
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_stream_kernel<FMT, NB, ROWS, NMAT, SINGLE>,
-                                                     256, lds) != hipSuccess || v <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &v, moe_stream_kernel<FMT, NB, ROWS, NMAT, SINGLE, LDSL>, 256, lds) != hipSuccess ||
+        v <= 0)
         v = 1;
     key[1] = key[0];
     val[1] = val[0];
@@ -945,11 +991,12 @@ int stage_blocks_per_cu(size_t lds) {
     return v;
 }
 
-// `max_group`: the most tokens any expert can receive in this call.
-template <int FMT, int NB, int ROWS, int NMAT>
-hipError_t launch_stage(MoeStage st, int64_t slots, int64_t max_group, hipStream_t s) {
+// `max_group`: the most tokens any expert can receive in this call.  LDSL: the
+// pair lists are rebuilt in LDS by every workgroup (st.inline_group).
+template <int FMT, int NB, int ROWS, int NMAT, bool LDSL>
+hipError_t launch_stage_l(MoeStage st, int64_t slots, int64_t max_group, hipStream_t s) {
     using C = MoeCfg<FMT, NB, ROWS, NMAT>;
-    const size_t lists = st.inline_group ? inline_group_bytes(st.e, st.p) : 0;
+    const size_t lists = LDSL ? inline_group_bytes(st.e, st.p) : 0;
     st.nchunk = (st.k + C::KC - 1) / C::KC;
     st.tiles = (int32_t)((st.n + ROWS - 1) / ROWS);
     const int64_t most = slots * st.tiles;
@@ -961,20 +1008,26 @@ hipError_t launch_stage(MoeStage st, int64_t slots, int64_t max_group, hipStream
     if constexpr (NB == 1) {
         const size_t lds1 = (size_t)C::kWBytes + C::kXBuf + lists;
         const int64_t cap1 =
-            (int64_t)stage_blocks_per_cu<FMT, NB, ROWS, NMAT, true>(lds1) * moe_device_cus();
+            (int64_t)stage_blocks_per_cu<FMT, NB, ROWS, NMAT, true, LDSL>(lds1) * moe_device_cus();
         if (st.nchunk == 1 && max_group <= NB && most <= cap1) {
-            hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT, true>), dim3((unsigned)most),
-                               dim3(256), lds1, s, st);
+            hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT, true, LDSL>),
+                               dim3((unsigned)most), dim3(256), lds1, s, st);
             return hipGetLastError();
         }
     }
     const size_t lds = C::kLds + lists;
-    const int per_cu = stage_blocks_per_cu<FMT, NB, ROWS, NMAT, false>(lds);
+    const int per_cu = stage_blocks_per_cu<FMT, NB, ROWS, NMAT, false, LDSL>(lds);
     const int64_t cap = (int64_t)per_cu * moe_device_cus();
     const unsigned grid = (unsigned)(most < cap ? most : cap);
-    hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT, false>), dim3(grid), dim3(256), lds,
-                       s, st);
+    hipLaunchKernelGGL((moe_stream_kernel<FMT, NB, ROWS, NMAT, false, LDSL>), dim3(grid),
+                       dim3(256), lds, s, st);
     return hipGetLastError();
+}
+
+template <int FMT, int NB, int ROWS, int NMAT>
+hipError_t launch_stage(const MoeStage& st, int64_t slots, int64_t max_group, hipStream_t s) {
+    return st.inline_group ? launch_stage_l<FMT, NB, ROWS, NMAT, true>(st, slots, max_group, s)
+                           : launch_stage_l<FMT, NB, ROWS, NMAT, false>(st, slots, max_group, s);
 }
 
 // Rows per tile.  One token (NB = 1): the most rows whose K chunk covers the
@@ -1000,19 +1053,20 @@ hipError_t launch_stage_rows(const MoeStage& st, int64_t slots, int64_t max_grou
     return launch_stage<FMT, NB, 32, NMAT>(st, slots, max_group, s);
 }
 
-template <int FMT, int NMAT>
-hipError_t launch_mstage(MoeMfma st, int64_t slots, hipStream_t s) {
+template <int FMT, int NMAT, bool LDSL>
+hipError_t launch_mstage_l(MoeMfma st, int64_t slots, hipStream_t s) {
     using M = MoeMCfg<FMT, NMAT>;
     using C = typename M::C;
-    const size_t lds = M::kLds + (st.inline_group ? inline_group_bytes(st.e, st.p) : 0);
+    const size_t lds = M::kLds + (LDSL ? inline_group_bytes(st.e, st.p) : 0);
     static size_t per_cu_lds = 0;
     static int per_cu = 0;
     if (per_cu_lds != lds) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_mfma_kernel<FMT, NMAT>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_mfma_kernel<FMT, NMAT, LDSL>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_mfma_kernel<FMT, NMAT>, 256, lds) !=
-                hipSuccess || v <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_mfma_kernel<FMT, NMAT, LDSL>, 256,
+                                                         lds) != hipSuccess ||
+            v <= 0)
             v = 1;
         per_cu = v;
         per_cu_lds = lds;
@@ -1022,8 +1076,14 @@ hipError_t launch_mstage(MoeMfma st, int64_t slots, hipStream_t s) {
     const int64_t most = slots * st.tiles;
     const int64_t cap = (int64_t)per_cu * moe_device_cus();
     const unsigned grid = (unsigned)(most < cap ? most : cap);
-    hipLaunchKernelGGL((moe_mfma_kernel<FMT, NMAT>), dim3(grid), dim3(256), lds, s, st);
+    hipLaunchKernelGGL((moe_mfma_kernel<FMT, NMAT, LDSL>), dim3(grid), dim3(256), lds, s, st);
     return hipGetLastError();
+}
+
+template <int FMT, int NMAT>
+hipError_t launch_mstage(const MoeMfma& st, int64_t slots, hipStream_t s) {
+    return st.inline_group ? launch_mstage_l<FMT, NMAT, true>(st, slots, s)
+                           : launch_mstage_l<FMT, NMAT, false>(st, slots, s);
 }
 
 // Split `rows` activation rows of K floats into the fragments at xf.
