@@ -203,7 +203,8 @@ int quant_gemm(int type, const void *w, int64_t n, int64_t k, const float *a, in
  *   idx    device int32 [T][top_k]
  *   probs  device fp32 [T][top_k]
  *   logits device fp32 [T][E], written (the selection is made on these values)
- *   1 <= top_k <= min(E, 32), 1 <= E <= 1024, H % 4 == 0.  T == 0 is a no-op.
+ *   1 <= top_k <= min(E, 32), 1 <= E <= 1024, H % 4 == 0, H <= 2^24.
+ *   T == 0 is a no-op.
  * Logits must be finite for the selection to be meaningful.
  * Errors: GGQ_ERR_ARG, GGQ_ERR_ALIGN.
  */

@@ -209,7 +209,7 @@ int quant_gemm(int type, const void* w, int64_t n, int64_t k, const float* a, in
 
 int moe_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t, int top_k,
               int32_t* idx, float* probs, float* logits, void* stream) {
-    if (e < 1 || e > kMaxExperts || h < 4 || h % 4 != 0 || t < 0) return GGQ_ERR_ARG;
+    if (e < 1 || e > kMaxExperts || h < 4 || h % 4 != 0 || h > (1 << 24) || t < 0) return GGQ_ERR_ARG;
     if (top_k < 1 || top_k > kMaxTopK || top_k > e) return GGQ_ERR_ARG;
     if (t > INT_MAX) return GGQ_ERR_ARG;
     if (t == 0) return GGQ_OK;

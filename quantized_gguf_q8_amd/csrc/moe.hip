@@ -79,6 +79,83 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
     }
 }
 
+// Prompt batches: a tile of 16 tokens x 8 experts per workgroup of 128
+// threads, thread (token tid/8, expert tid%8), so that a 512-token batch gives
+// two workgroups per compute unit.  Columns are staged through LDS 512 at a
+// time (the next chunk's rows fetched into registers while the current one is
+// used), so each token row and router row is read once per tile instead of
+// once per (expert, token group); chunks are long because each one costs a
+// memory round trip that only its own compute can hide.  Each thread keeps four component sums over
+// 64 columns and adds them to its total every 64 columns (error within about
+// 24 rounding units of sum |w x|).
+constexpr int kRTT = 16;    // tokens per tile
+constexpr int kRTE = 8;     // experts per tile
+constexpr int kRKC = 512;   // columns per staged chunk
+constexpr int kRRow = kRKC + 4;   // LDS row stride in floats
+
+__global__ __launch_bounds__(128) void router_tile_kernel(const float* __restrict__ wr, int64_t e,
+                                                          int64_t h, const float* __restrict__ x,
+                                                          int64_t t, float* __restrict__ logits) {
+    __shared__ __align__(16) float xs[kRTT * kRRow];
+    __shared__ __align__(16) float ws[kRTE * kRRow];
+    const int tid = threadIdx.x;
+    const int tt = tid / kRTE, te = tid % kRTE;
+    const int64_t e0 = (int64_t)blockIdx.x * kRTE;
+    // staging: thread loads float4 c = tid (of the chunk's 128) of every row,
+    // as buffer loads over the tile's rows: rows past t or e and columns past h
+    // read zeros without a select on the loaded value
+    const int sc = tid;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(wr + e0 * h, (uint32_t)((e - e0 < kRTE ? e - e0 : kRTE) * h * 4));
+    // token tiles blockIdx.y, + gridDim.y, ... (the grid's y extent is capped)
+    for (int64_t t0 = (int64_t)blockIdx.y * kRTT; t0 < t; t0 += (int64_t)gridDim.y * kRTT) {
+        const __amdgpu_buffer_rsrc_t rx =
+            make_rsrc(x + t0 * h, (uint32_t)((t - t0 < kRTT ? t - t0 : kRTT) * h * 4));
+        float4 xv[kRTT], wv[kRTE];
+        auto fetch = [&](int64_t k0) {
+            const int64_t k = k0 + 4 * sc;
+#pragma unroll
+            for (int i = 0; i < kRTT; ++i)
+                xv[i] = __builtin_bit_cast(float4, buf_load16<false>(
+                    rx, k < h ? (uint32_t)((i * h + k) * 4) : kOob));
+#pragma unroll
+            for (int i = 0; i < kRTE; ++i)
+                wv[i] = __builtin_bit_cast(float4, buf_load16<false>(
+                    rw, k < h ? (uint32_t)((i * h + k) * 4) : kOob));
+        };
+        float total = 0.f;
+        fetch(0);
+        for (int64_t k0 = 0; k0 < h; k0 += kRKC) {
+#pragma unroll
+            for (int i = 0; i < kRTT; ++i)
+                *reinterpret_cast<float4*>(xs + i * kRRow + 4 * sc) = xv[i];
+#pragma unroll
+            for (int i = 0; i < kRTE; ++i)
+                *reinterpret_cast<float4*>(ws + i * kRRow + 4 * sc) = wv[i];
+            __syncthreads();
+            fetch(k0 + kRKC);   // past h: reads nothing
+            const float* xr = xs + tt * kRRow;
+            const float* wrow = ws + te * kRRow;
+#pragma unroll
+            for (int q = 0; q < kRKC / 64; ++q) {
+                float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const float4 a = *reinterpret_cast<const float4*>(xr + 64 * q + 4 * c);
+                    const float4 b = *reinterpret_cast<const float4*>(wrow + 64 * q + 4 * c);
+                    p[0] += a.x * b.x;
+                    p[1] += a.y * b.y;
+                    p[2] += a.z * b.z;
+                    p[3] += a.w * b.w;
+                }
+                total += (p[0] + p[1]) + (p[2] + p[3]);
+            }
+            __syncthreads();
+        }
+        if (t0 + tt < t && e0 + te < e) logits[(t0 + tt) * e + e0 + te] = total;
+    }
+}
+
 // One wave per token.  The top_k logits (ties -> lower index) are found by a
 // radix select over order-preserving 32-bit keys: 32 rounds, each counting
 // with wave ballots how many keys lie above a candidate threshold, so no
@@ -1201,10 +1278,17 @@ hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* w
 
 hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t,
                         int top_k, int32_t* idx, float* probs, float* logits, hipStream_t s) {
-    const int64_t groups = (t + 3) / 4;
-    hipLaunchKernelGGL(router_logits_kernel,
-                       dim3((unsigned)((e + 3) / 4), (unsigned)(groups < 64 ? groups : 64)),
-                       dim3(256), 0, s, wr, e, h, x, t, logits);
+    if (t >= 32) {
+        const int64_t tiles = (t + kRTT - 1) / kRTT;
+        hipLaunchKernelGGL(router_tile_kernel,
+                           dim3((unsigned)((e + kRTE - 1) / kRTE), (unsigned)(tiles < 65535 ? tiles : 65535)),
+                           dim3(128), 0, s, wr, e, h, x, t, logits);
+    } else {
+        const int64_t groups = (t + 3) / 4;
+        hipLaunchKernelGGL(router_logits_kernel,
+                           dim3((unsigned)((e + 3) / 4), (unsigned)(groups < 64 ? groups : 64)),
+                           dim3(256), 0, s, wr, e, h, x, t, logits);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (e <= 128)

@@ -174,6 +174,7 @@ def test_route_validation(g):
     assert L.moe_route(A16, 4, 2048, B16, 1, 5, C16, D16, D16, None) == ARG
     assert L.moe_route(A16, 2048, 2048, B16, 1, 8, C16, D16, D16, None) == ARG
     assert L.moe_route(A16, 128, 2046, B16, 1, 8, C16, D16, D16, None) == ARG
+    assert L.moe_route(A16, 128, (1 << 24) + 4, B16, 1, 8, C16, D16, D16, None) == ARG
     assert L.moe_route(A16, 128, 2048, B16, 1, 8, C16, D16, None, None) == ARG
     assert L.moe_route(A16 + 4, 128, 2048, B16, 1, 8, C16, D16, D16, None) == ALIGN
     assert L.moe_route(None, 128, 2048, None, 0, 8, None, None, None, None) == OK

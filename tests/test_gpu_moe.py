@@ -52,8 +52,10 @@ def _route_checks(g, wr, x, k):
     return idx, probs, near
 
 
-@pytest.mark.parametrize("t", [1, 16, 64])
+@pytest.mark.parametrize("t", [1, 16, 33, 64, 512])
 def test_route_moe_router(g, t):
+    """1 and 16 tokens: one wave per expert; from 32 tokens: 16x16 tiles (33:
+    a ragged last tile; 512: the prompt batch)."""
     say(f"route t={t}")
     mo = synth.moe_layer(seed=0, n_tokens=t)
     _, _, near = _route_checks(g, mo["wr"], mo["x"], synth.MOE_TOP_K)
@@ -92,6 +94,16 @@ def test_route_many_experts(g, e, k):
     x = np.round(synth.normal_f32((5, h), seed=2, tensor_id=8) * 4) / 4
     idx, _, _ = _route_checks(g, wr, x.astype(np.float32), k)
     assert all(len(set(r)) == k for r in idx)
+
+
+def test_route_tiles_ragged(g):
+    """The tiled router with experts and columns that fill no tile or chunk
+    evenly (E = 37, H = 300) and 50 tokens."""
+    say("route tiles ragged")
+    e, h, t = 37, 300, 50
+    wr = synth.normal_f32((e, h), seed=3, tensor_id=9, std=0.05)
+    x = synth.normal_f32((t, h), seed=3, tensor_id=10)
+    _route_checks(g, wr, x, 6)
 
 
 def _moe_bound(fmt, mo, x, idx, probs, e, h, f):
