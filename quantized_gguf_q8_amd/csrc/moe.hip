@@ -858,8 +858,11 @@ struct MoeMPrefetch {
             const int64_t r = u.r0 + qm / M::PPR;
             const uint32_t off = (uint32_t)(qm % M::PPR) * 16;
             const bool ok = m < NMAT && qm < M::WMP && r < st.n && cb0 + off < st.rb;
-            const uint8_t* src = st.w[m < NMAT ? m : 0] + ((int64_t)u.e * st.n + (ok ? r : 0)) * st.rb +
-                                 (ok ? cb0 + off : 0);
+            // a select between the two (scalar) matrix pointers: indexing the
+            // argument array with a per-lane index would load the pointer from
+            // memory, and every weight address would wait for it
+            const uint8_t* mat = m == 1 ? st.w[NMAT - 1] : st.w[0];
+            const uint8_t* src = mat + ((int64_t)u.e * st.n + (ok ? r : 0)) * st.rb + (ok ? cb0 + off : 0);
             w[i] = load_once16(src);
             wok |= (uint32_t)ok << i;
         }
