@@ -20,7 +20,7 @@
 //   4. down    : per (tile, 128 rows of H): d = Wd h, written in fp32 to the row
 //                of the slot's pair.
 //   5. combine : y[t] = sum_s probs[t][s] * d_(t,s) in slot order.
-// Kernels 3 and 4 are the same code.  A workgroup of four waves holds one tile;
+// Kernels 3 and 4 are the same code.  A workgroup of kMgWaves waves holds one tile;
 // the tile's bf16 activations are staged through LDS 256 columns at a time and
 // shared by the waves, while each wave decodes its own 16-row column tiles of
 // the quantized weights straight into matrix-core operands (no LDS round trip
@@ -60,6 +60,7 @@ constexpr int kBM = 64;      // slots per tile (four 16-row groups)
 constexpr int kKC = 256;     // columns per chunk
 constexpr int kAFrag = 1024; // bytes of one 16x32 bf16 operand fragment
 constexpr int kABuf = 8 * 4 * kAFrag;   // one chunk: 8 products x 4 groups
+constexpr int kMgWaves = 4;  // waves per workgroup of the grouped products
 
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
@@ -252,10 +253,16 @@ __host__ __device__ constexpr int mg_kcol(int q, int s) {
                         : 64 * q + 8 * s;
 }
 
-// Per-chunk constants of a lane's weights (w = a*q + b): Q4_K its four
-// sub-blocks 2(q/2), +1, +4, +5; Q8_0 its two blocks (q + 128 read unsigned).
+// Per-chunk constants of a lane's weights: Q4_K its four sub-blocks
+// 2(q/2), +1, +4, +5 (w = a*q + b with a = d*sc, b = -dmin*m); Q8_0 its two
+// blocks (w = a*u - 128a, u = q + 128 read unsigned).  The decode takes each
+// quant byte v as the exact fp16 value 1024 + v (exponent byte 0x64 placed by a
+// byte permute, two per instruction) and forms w = a*(1024 + v) + c with
+// c = b - 1024a in one mixed-precision FMA.  Q8_0: both products are exact, so w
+// is the same fp32 value as a*u - 128a.  Q4_K: c is rounded once, an error of
+// at most 2^-14 |a| before w is rounded to bf16.
 struct MgScale {
-    float a[4], b[4];
+    float a[4], c[4];
 };
 
 template <int FMT>
@@ -274,15 +281,15 @@ __device__ __forceinline__ MgScale mg_scales(const MgRaw<FMT>& r, int q) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             s.a[i] = d * (float)sc_[i];
-            s.b[i] = -dmin * (float)m_[i];
+            s.c[i] = -dmin * (float)m_[i] - 1024.f * s.a[i];
         }
     } else {
         (void)q;
         s.a[0] = half_bits_to_float(r.v0.x);
-        s.b[0] = -128.f * s.a[0];
+        s.c[0] = -1152.f * s.a[0];
         s.a[1] = half_bits_to_float(r.v2.x >> 16);   // bytes 34-35
-        s.b[1] = -128.f * s.a[1];
-        s.a[2] = s.a[3] = s.b[2] = s.b[3] = 0.f;
+        s.c[1] = -1152.f * s.a[1];
+        s.a[2] = s.a[3] = s.c[2] = s.c[3] = 0.f;
     }
     return s;
 }
@@ -295,7 +302,7 @@ __device__ __forceinline__ uint32_t u4_at(const u32x4& v, int i) {
 template <int FMT, int S>
 __device__ __forceinline__ bf16x8 mg_decode(const MgRaw<FMT>& r, const MgScale& sc) {
     uint32_t w0, w1;
-    float a, b;
+    float a, c;
     if constexpr (FMT == kQ4_K) {
         // bytes 8(S%2) .. +7 of the lane's first (S < 4) or second 16 quant
         // bytes; low nibbles for S%4 < 2, high after
@@ -311,11 +318,10 @@ __device__ __forceinline__ bf16x8 mg_decode(const MgRaw<FMT>& r, const MgScale& 
             w1 = opaque((x1 >> 4) & 0x0F0F0F0Fu);
         }
         a = sc.a[sb];
-        b = sc.b[sb];
+        c = sc.c[sb];
     } else {
         // bytes of the lane's 68: block 2q quants at 2..33, block 2q+1 at 36..67.
-        // (q ^ 0x80) read as an unsigned byte is q + 128; a*(q+128) - 128a = a*q
-        // exactly (both products fit in fp32's mantissa).
+        // (q ^ 0x80) read as an unsigned byte is q + 128.
         const uint32_t d[17] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w,
                                 r.v2.x, r.v2.y, r.v2.z, r.v2.w, r.v3.x, r.v3.y, r.v3.z, r.v3.w,
                                 r.v4};
@@ -323,21 +329,28 @@ __device__ __forceinline__ bf16x8 mg_decode(const MgRaw<FMT>& r, const MgScale& 
             w0 = __builtin_amdgcn_alignbyte(d[2 * S + 1], d[2 * S], 2);
             w1 = __builtin_amdgcn_alignbyte(d[2 * S + 2], d[2 * S + 1], 2);
             a = sc.a[0];
-            b = sc.b[0];
+            c = sc.c[0];
         } else {
             w0 = d[9 + 2 * (S - 4)];
             w1 = d[10 + 2 * (S - 4)];
             a = sc.a[1];
-            b = sc.b[1];
+            c = sc.c[1];
         }
         w0 ^= 0x80808080u;
         w1 ^= 0x80808080u;
     }
+    // bytes -> fp16 1024 + v, two per permute (byte 4 of the selector is 0x64)
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    constexpr uint32_t e = 0x64646464u;
+    const h2 p0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(e, w0, 0x04010400u));
+    const h2 p1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(e, w0, 0x04030402u));
+    const h2 p2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(e, w1, 0x04010400u));
+    const h2 p3 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(e, w1, 0x04030402u));
     u32x4 o;
-    o.x = cvt_bf16x2(__builtin_fmaf(a, ubyte_f(w0, 0), b), __builtin_fmaf(a, ubyte_f(w0, 1), b));
-    o.y = cvt_bf16x2(__builtin_fmaf(a, ubyte_f(w0, 2), b), __builtin_fmaf(a, ubyte_f(w0, 3), b));
-    o.z = cvt_bf16x2(__builtin_fmaf(a, ubyte_f(w1, 0), b), __builtin_fmaf(a, ubyte_f(w1, 1), b));
-    o.w = cvt_bf16x2(__builtin_fmaf(a, ubyte_f(w1, 2), b), __builtin_fmaf(a, ubyte_f(w1, 3), b));
+    o.x = cvt_bf16x2(__builtin_fmaf(a, (float)p0.x, c), __builtin_fmaf(a, (float)p0.y, c));
+    o.y = cvt_bf16x2(__builtin_fmaf(a, (float)p1.x, c), __builtin_fmaf(a, (float)p1.y, c));
+    o.z = cvt_bf16x2(__builtin_fmaf(a, (float)p2.x, c), __builtin_fmaf(a, (float)p2.y, c));
+    o.w = cvt_bf16x2(__builtin_fmaf(a, (float)p3.x, c), __builtin_fmaf(a, (float)p3.y, c));
     return __builtin_bit_cast(bf16x8, o);
 }
 
@@ -352,8 +365,9 @@ __device__ __forceinline__ int mg_lds_off(int s, int g, int l) {
 // One tile (G 16-row groups of slots, G fixed at compile time so that the
 // inner loops carry no per-product branch) against 64*TPW rows of each matrix.
 // NMAT = 2: gate and up (wave w holds rows 16*(w*TPW + j) .. of both
-// matrices); NMAT = 1: one matrix.  Four waves per workgroup.
-template <int FMT, int NMAT, int TPW, int G>
+// matrices); NMAT = 1: one matrix.  NW waves per workgroup (4 and 8 measured
+// the same; 4 is used).
+template <int FMT, int NMAT, int TPW, int NW, int G>
 __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0, int ex, int nt) {
     constexpr int NT = NMAT * TPW;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -369,19 +383,20 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     int64_t col[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-        col[j] = (int64_t)nt * (64 * TPW) + 16 * (wave * TPW + j) + (lane & 15);
+        col[j] = (int64_t)nt * (16 * TPW * NW) + 16 * (wave * TPW + j) + (lane & 15);
         roff[j] = col[j] < p.n ? (uint32_t)(col[j] * p.rb) : kOob;
     }
 
-    // activation staging: thread pieces i = 0..2G-1 are row tid/32 + 8i, piece
-    // u = tid % 32 (product u % 8, lane group u / 8) of that row's chunk
+    // activation staging: thread pieces i = 0..PPT-1 are row tid/32 + 2*NW*i,
+    // piece u = tid % 32 (product u % 8, lane group u / 8) of that row's chunk
+    constexpr int PPT = 8 * G / NW;   // 16G rows x 32 pieces over 64*NW threads
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.abytes);
     const int u = tid & 31, us = u & 7, uq = u >> 3;
     const uint32_t acol = (uint32_t)(2 * mg_kcol<FMT>(uq, us));
-    uint32_t asrc[2 * G];   // byte offset of the row's first chunk, or kOob
+    uint32_t asrc[PPT];   // byte offset of the row's first chunk, or kOob
 #pragma unroll
-    for (int i = 0; i < 2 * G; ++i) {
-        const int slot = row0 + (tid >> 5) + 8 * i;
+    for (int i = 0; i < PPT; ++i) {
+        const int slot = row0 + (tid >> 5) + 2 * NW * i;
         int src = slot;
         if (p.adiv > 0) {
             const int pr = p.spair[slot];
@@ -389,21 +404,24 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
         }
         asrc[i] = src >= 0 ? (uint32_t)src * (uint32_t)p.k * 2u + acol : kOob;
     }
-    // LDS destination of piece i: row r = tid/32 + 8i has group i/2 and row
-    // (tid/32) + 8(i%2) within it, so the offsets differ by constants
+    // LDS destination of piece i: row r = tid/32 + 2*NW*i lies in group r/16 at
+    // row r%16, so the offsets differ from piece 0's by constants
     const int adst0 = mg_lds_off(us, 0, (tid >> 5) + 16 * uq);
-    u32x4 av[2 * G];
+    auto adst = [&](int i) {
+        return NW == 8 ? adst0 + i * kAFrag : adst0 + (i >> 1) * kAFrag + (i & 1) * 128;
+    };
+    u32x4 av[PPT];
+    const int nc = p.k / kKC;
     auto load_a = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < 2 * G; ++i) {
+        for (int i = 0; i < PPT; ++i) {
             const uint32_t off = asrc[i] == kOob ? kOob : asrc[i] + (uint32_t)c * (kKC * 2);
             av[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
         }
     };
     auto store_a = [&](uint8_t* buf) {
 #pragma unroll
-        for (int i = 0; i < 2 * G; ++i)
-            *reinterpret_cast<u32x4*>(buf + adst0 + (i >> 1) * kAFrag + (i & 1) * 128) = av[i];
+        for (int i = 0; i < PPT; ++i) *reinterpret_cast<u32x4*>(buf + adst(i)) = av[i];
     };
 
     MgRaw<FMT> rw[2][NT];
@@ -461,7 +479,6 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     // branch around them would leave the wait counter unknown at the join, and
     // the compiler would then wait for the prefetch before using the current
     // chunk.  The last chunk (no successor) is peeled off.
-    const int nc = p.k / kKC;
     load_a(0);
     load_w(0, rw[0]);
     store_a(lds);
@@ -512,8 +529,8 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     }
 }
 
-template <int FMT, int NMAT, int TPW>
-__global__ __launch_bounds__(256, 2) void mg_kernel(const MgArgs p) {
+template <int FMT, int NMAT, int TPW, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void mg_kernel(const MgArgs p) {
     extern __shared__ __align__(16) uint8_t lds[];
     // blocks go to the eight XCDs round robin: XCD x takes tiles x, x+8, ...,
     // each with all its column tiles in a row, so a tile's activations are
@@ -527,24 +544,25 @@ __global__ __launch_bounds__(256, 2) void mg_kernel(const MgArgs p) {
     const int tinfo = p.tiles[2 * mt + 1];
     const int ex = tinfo >> 3;
     switch (tinfo & 7) {   // 16-row groups in this tile (1..4)
-        case 1: mg_tile<FMT, NMAT, TPW, 1>(p, lds, row0, ex, nt); break;
-        case 2: mg_tile<FMT, NMAT, TPW, 2>(p, lds, row0, ex, nt); break;
-        case 3: mg_tile<FMT, NMAT, TPW, 3>(p, lds, row0, ex, nt); break;
-        default: mg_tile<FMT, NMAT, TPW, 4>(p, lds, row0, ex, nt); break;
+        case 1: mg_tile<FMT, NMAT, TPW, NW, 1>(p, lds, row0, ex, nt); break;
+        case 2: mg_tile<FMT, NMAT, TPW, NW, 2>(p, lds, row0, ex, nt); break;
+        case 3: mg_tile<FMT, NMAT, TPW, NW, 3>(p, lds, row0, ex, nt); break;
+        default: mg_tile<FMT, NMAT, TPW, NW, 4>(p, lds, row0, ex, nt); break;
     }
 }
 
-template <int FMT, int NMAT, int TPW>
+template <int FMT, int NMAT, int TPW, int NW>
 hipError_t launch_mg(MgArgs a, int64_t tile_bound, hipStream_t s) {
     static bool attr = false;
     if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(mg_kernel<FMT, NMAT, TPW>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(mg_kernel<FMT, NMAT, TPW, NW>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kABuf);
         attr = true;
     }
-    a.ntn = (int32_t)((a.n + 64 * TPW - 1) / (64 * TPW));
+    constexpr int rows = 16 * TPW * NW;   // rows of each matrix per workgroup
+    a.ntn = (int32_t)((a.n + rows - 1) / rows);
     const int64_t mt8 = (tile_bound + 7) / 8 * 8;
-    hipLaunchKernelGGL((mg_kernel<FMT, NMAT, TPW>), dim3((unsigned)(mt8 * a.ntn)), dim3(256),
+    hipLaunchKernelGGL((mg_kernel<FMT, NMAT, TPW, NW>), dim3((unsigned)(mt8 * a.ntn)), dim3(64 * NW),
                        2 * kABuf, s, a);
     return hipGetLastError();
 }
@@ -568,7 +586,7 @@ hipError_t launch_fmt(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, i
     a.spair = m.spair;
     a.hout = m.hb;
     a.ldo = f;
-    hipError_t err = launch_mg<FMT, 2, 1>(a, tb, s);
+    hipError_t err = launch_mg<FMT, 2, 1, kMgWaves>(a, tb, s);
     if (err != hipSuccess) return err;
     MgArgs d{};
     d.w[0] = wd;
@@ -584,7 +602,7 @@ hipError_t launch_fmt(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, i
     d.spair = m.spair;
     d.dout = m.dbuf;
     d.ldo = h;
-    return launch_mg<FMT, 1, 2>(d, tb, s);
+    return launch_mg<FMT, 1, 2, kMgWaves>(d, tb, s);
 }
 
 }  // namespace
