@@ -148,46 +148,69 @@ __device__ __forceinline__ void load_unit(const WView& v, int64_t row, int k0, i
     }
 }
 
-// Decode one unit into 16 bf16 weights of LDS row `dst` (bf16 elements).
+// Four quant bytes v -> w = a*(1024 + v) + c as four bf16 (two packed words).
+// A byte permute places each byte under the exponent byte 0x64, which makes the
+// exact fp16 value 1024 + v (two per instruction); one mixed-precision FMA per
+// weight then gives a*v + b with c = b - 1024a.
+__device__ __forceinline__ void decode4(uint32_t v, float a, float c, uint32_t& o0, uint32_t& o1) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    constexpr uint32_t e = 0x64646464u;
+    const h2 p0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(e, v, 0x04010400u));
+    const h2 p1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(e, v, 0x04030402u));
+    o0 = cvt_bf16x2(__builtin_fmaf(a, (float)p0.x, c), __builtin_fmaf(a, (float)p0.y, c));
+    o1 = cvt_bf16x2(__builtin_fmaf(a, (float)p1.x, c), __builtin_fmaf(a, (float)p1.y, c));
+}
+
+// Decode one unit into 16 bf16 weights of LDS row `dst` (bf16 elements).  For
+// Q4_K, g = (step) % 4 is the step's 64-weight group of its super-block; the
+// callers pass it as a constant so that the scale and min extraction of the two
+// sub-blocks 2g, 2g+1 is a handful of fixed bit-field reads.
 template <int FMT>
-__device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int k0, uint16_t* dst) {
+__device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int g, uint16_t* dst) {
     if constexpr (FMT == kQ4_K) {
-        const int g = (k0 / 64) & 3;
+        // packed scales s[0..11] = hdr.y, hdr.z, hdr.w.  Sub-block j < 4: scale
+        // s[j] & 63, min s[j+4] & 63; j >= 4: scale low nibble of s[j+4] with the
+        // top two bits of s[j-4], min high nibble of s[j+4] with those of s[j].
+        uint32_t sc0, m0, sc1, m1;
+        if (g < 2) {
+            const int sh = 16 * g;
+            sc0 = (r.hdr.y >> sh) & 63u;
+            sc1 = (r.hdr.y >> (sh + 8)) & 63u;
+            m0 = (r.hdr.z >> sh) & 63u;
+            m1 = (r.hdr.z >> (sh + 8)) & 63u;
+        } else {
+            const int sh = 16 * (g - 2);
+            sc0 = ((r.hdr.w >> sh) & 15u) | (((r.hdr.y >> (sh + 6)) & 3u) << 4);
+            sc1 = ((r.hdr.w >> (sh + 8)) & 15u) | (((r.hdr.y >> (sh + 14)) & 3u) << 4);
+            m0 = ((r.hdr.w >> (sh + 4)) & 15u) | (((r.hdr.z >> (sh + 6)) & 3u) << 4);
+            m1 = ((r.hdr.w >> (sh + 12)) & 15u) | (((r.hdr.z >> (sh + 14)) & 3u) << 4);
+        }
         const float d = half_bits_to_float(r.hdr.x);
         const float dmin = half_bits_to_float(r.hdr.x >> 16);
-        const Q4KScales sc = q4k_unpack(r.hdr.y, r.hdr.z, r.hdr.w);
-        uint32_t sc0, m0, sc1, m1;
-        q4k_sub(sc, 2 * g, sc0, m0);
-        q4k_sub(sc, 2 * g + 1, sc1, m1);
-        const float a0 = d * (float)sc0, b0 = -dmin * (float)m0;
-        const float a1 = d * (float)sc1, b1 = -dmin * (float)m1;
+        const float a0 = d * (float)sc0, a1 = d * (float)sc1;
+        const float c0 = -dmin * (float)m0 - 1024.f * a0;
+        const float c1 = -dmin * (float)m1 - 1024.f * a1;
         const uint32_t qw[2] = {r.q0, r.q1};
         uint32_t lo[4], hi[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const uint32_t l = opaque(qw[i] & 0x0F0F0F0Fu);
-            const uint32_t h = opaque((qw[i] >> 4) & 0x0F0F0F0Fu);
-            lo[2 * i] = cvt_bf16x2(__builtin_fmaf(a0, ubyte_f(l, 0), b0), __builtin_fmaf(a0, ubyte_f(l, 1), b0));
-            lo[2 * i + 1] = cvt_bf16x2(__builtin_fmaf(a0, ubyte_f(l, 2), b0), __builtin_fmaf(a0, ubyte_f(l, 3), b0));
-            hi[2 * i] = cvt_bf16x2(__builtin_fmaf(a1, ubyte_f(h, 0), b1), __builtin_fmaf(a1, ubyte_f(h, 1), b1));
-            hi[2 * i + 1] = cvt_bf16x2(__builtin_fmaf(a1, ubyte_f(h, 2), b1), __builtin_fmaf(a1, ubyte_f(h, 3), b1));
+            decode4(opaque(qw[i] & 0x0F0F0F0Fu), a0, c0, lo[2 * i], lo[2 * i + 1]);
+            decode4(opaque((qw[i] >> 4) & 0x0F0F0F0Fu), a1, c1, hi[2 * i], hi[2 * i + 1]);
         }
         *reinterpret_cast<uint4*>(dst + 8 * u) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         *reinterpret_cast<uint4*>(dst + 32 + 8 * u) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     } else {
-        (void)k0;
-        // (q ^ 0x80) read as an unsigned byte is q + 128; d*(q+128) - 128d = d*q
-        // exactly (both products fit in fp32's mantissa).
+        (void)g;
+        // (q ^ 0x80) read as an unsigned byte is u = q + 128, and d*q =
+        // d*(1024 + u) - 1152d exactly (both products fit in fp32's mantissa).
         const float d = half_bits_to_float(r.d);
-        const float nd = -128.f * d;
+        const float c = -1152.f * d;
         const uint32_t xs[5] = {r.x.x, r.x.y, r.x.z, r.x.w, r.x4};
         uint32_t o[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t qd = __builtin_amdgcn_alignbyte(xs[i + 1], xs[i], r.sh) ^ 0x80808080u;
-            o[2 * i] = cvt_bf16x2(__builtin_fmaf(d, ubyte_f(qd, 0), nd), __builtin_fmaf(d, ubyte_f(qd, 1), nd));
-            o[2 * i + 1] = cvt_bf16x2(__builtin_fmaf(d, ubyte_f(qd, 2), nd), __builtin_fmaf(d, ubyte_f(qd, 3), nd));
-        }
+        for (int i = 0; i < 4; ++i)
+            decode4(__builtin_amdgcn_alignbyte(xs[i + 1], xs[i], r.sh) ^ 0x80808080u, d, c,
+                    o[2 * i], o[2 * i + 1]);
         uint4* d4 = reinterpret_cast<uint4*>(dst + 16 * u);
         d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
         d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -268,21 +291,24 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
     // of the step together, so a load instruction touches few cache lines
     RawUnit<FMT> ru[kDW][S::UPT];
 
-    // The loop body is unrolled kDW times so that every register ring index is a
-    // compile-time constant; the step count is rounded up to a multiple of kDW
-    // and the extra steps multiply zeros (their A loads lie past the
-    // descriptor's range), so no step needs a branch or a variable wait count.
-    const int nsteps = (nk + kDW - 1) / kDW * kDW;
+    // The loop body is unrolled kDW = 4 times so that every register ring index
+    // and every step's position in its super-block is a compile-time constant;
+    // the host makes a split's step count a multiple of 4, so no step needs a
+    // branch or a variable wait count.  Loads ahead of the last step read the
+    // last step again and are never used.
+    static_assert(kDW == 4, "the decode takes a step's super-block group from the unroll index");
+    const int nsteps = nk;
+    // The step offset is uniform and goes in the scalar offset, so an A load
+    // costs no vector instruction.  The load after the last step (issued by the
+    // last step, never used) reads the last step again.
     auto load_a = [&](int ks, bf16x8 (&dst)[2][4]) {
-        const bool valid = ks < nk;
-        const uint32_t kb = (uint32_t)(kstep0 + ks) * astep;
+        const uint32_t kb = (uint32_t)(kstep0 + min(ks, nk - 1)) * astep;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 dst[h][i] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                ra, valid ? aoff[i] + kb + 1024 * h : kOob, 0, 0));
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] + 1024 * h, kb, 0));
     };
     // Lanes past a wave's share load a valid unit too (and never store it).
     auto unit_of = [&](int i) {
@@ -297,14 +323,16 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
             load_unit<FMT>(wv, n0 + q / 4, step * kBK, q % 4, dst[i]);
         }
     };
-    auto store_w = [&](int ks, const RawUnit<FMT> (&src)[S::UPT], uint16_t* buf) {
-        const int step = kstep0 + min(ks, nk - 1);
+    // g = the step's index mod 4, a constant at every call (kstep0 and the
+    // unrolled loop's base step are multiples of 4, and nk is too, so no step
+    // is clamped)
+    auto store_w = [&](int g, const RawUnit<FMT> (&src)[S::UPT], uint16_t* buf) {
 #pragma unroll
         for (int i = 0; i < S::UPT; ++i) {
             const int qi = lane + 64 * i;
             const int q = S::UPW * wave + qi;
             const int row = (qi < S::UPW && q < S::UNITS) ? q / 4 : S::BN;
-            store_unit<FMT>(src[i], q % 4, step * kBK, buf + row * kLRow);
+            store_unit<FMT>(src[i], q % 4, g, buf + row * kLRow);
         }
     };
 
@@ -342,7 +370,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
                                                                             acc[i][j], 0, 0, 0);
                 }
             }
-            store_w(ks + 1, ru[(d + 1) % kDW], wl + ((d + 1) & 1) * S::kBuf);
+            store_w((d + 1) % kDW, ru[(d + 1) % kDW], wl + ((d + 1) & 1) * S::kBuf);
             __syncthreads();
         }
     }
@@ -492,7 +520,9 @@ hipError_t launch_gemm(int type, const uint8_t* w, int64_t n, int64_t k, const f
     g.tiles_n = pl.tiles_n;
     g.splits = pl.splits;
     const int ksteps = (int)(kp / kBK);
-    g.ksteps_per_split = (ksteps + pl.splits - 1) / pl.splits;
+    // a multiple of 4 steps per split (the kernel's decode takes the step's
+    // position in its super-block from the unrolled loop index); ksteps is one
+    g.ksteps_per_split = ((ksteps + pl.splits - 1) / pl.splits + 3) / 4 * 4;
     err = type == kQ4_K ? launch_fmt<kQ4_K>(g, pl, s) : launch_fmt<kQ8_0>(g, pl, s);
     if (err != hipSuccess || pl.splits == 1) return err;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((m * n + 255) / 256)), dim3(256), 0, s,
