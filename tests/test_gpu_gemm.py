@@ -25,9 +25,13 @@ def g():
     return g
 
 
+# The last three split K eight or four ways with step counts that leave the
+# last splits short or empty (each split takes a multiple of 4 of the 64-wide
+# steps: 68 steps -> 12 x 5 + 8 + 0 + 0; 132 -> 20 x 6 + 12 + 0; 36 -> 12 x 3 + 0).
 @pytest.mark.parametrize("fmt,m,n,k", [
     (Q4, 37, 70, 512), (Q8, 130, 200, 1056), (Q8, 1, 64, 64), (Q4, 129, 257, 2560),
     (Q8, 512, 300, 2048), (Q4, 3, 17, 256),
+    (Q4, 40, 96, 4352), (Q8, 24, 48, 8448), (Q4, 64, 64, 2304),
 ])
 def test_gemm_parity_full_check(g, fmt, m, n, k):
     say(f"gemm fmt={fmt} m={m} n={n} k={k}")
