@@ -230,8 +230,8 @@ size_t moe_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f)
  * e*F*(H/256)*144, expert e of Wd (H x F) at byte e*H*(F/256)*144.
  *   type   GGQ_Q4_K or GGQ_Q8_0; H and F multiples of 256; T*top_k <= 65536
  *   x      device fp32 [T][H];  y device fp32 [T][H]
- *   idx    device int32 [T][top_k], each in [0, E) (out-of-range entries are
- *          treated as expert 0 with weight 0 -- never read out of bounds)
+ *   idx    device int32 [T][top_k], each in [0, E) (out-of-range entries get
+ *          weight 0 and are never read out of bounds)
  *   probs  device fp32 [T][top_k]
  *   ws     device workspace >= moe_workspace_size(E, T, top_k, H, F) bytes,
  *          256-byte aligned.  On return ws holds h at byte offset

@@ -23,8 +23,12 @@
 //                epilogue h = silu(g) * u (matrix cores from two tokens on).
 //   3. down    : per (selected expert, row tile): d = Wd h for each of its pairs.
 //   4. combine : y[t] = sum_s probs[t][s] * d_(t,s) in slot order.
+// For one token, 3 and 4 are one kernel (per row tile of H: every slot's down
+// product, then the weighted sum in slot order).
 // Only the selected experts' bytes are read, once per group of up to 16 tokens
 // routed to the expert, and nothing is accumulated with atomics.
+#include <algorithm>
+
 #include "gemv_mfma_core.h"
 #include "ggq_launch.h"
 
@@ -1039,6 +1043,160 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     y[ti * hdim + r] = acc;
 }
 
+// ------------------------------------------ one token: down and combine ----
+// y = sum over slots s, in slot order, of probs[s] * (Wd[idx[s]] h_s) in one
+// launch, for one token (no per-slot rows written, no combine launch).  A
+// workgroup owns `rows` rows of H and every unit (slot, row, 64-weight piece
+// of F) of them, at most kD1Units per thread, all fetched at once; the h of
+// every slot is staged in LDS once.  A unit's partial sum goes to LDS and the
+// row's owner adds them up in (slot, piece) order.  Slots whose expert index
+// lies outside [0, E) contribute nothing and their weights are not read.
+constexpr int kD1Units = 4;
+
+struct Down1Args {
+    const uint8_t* wd;     // [E][H][rb]
+    const float* h;        // [top_k][F]
+    const int32_t* idx;    // [top_k]
+    const float* probs;    // [top_k]
+    float* y;              // [H]
+    int64_t e, hdim, rb;   // experts, rows of H, bytes per row of Wd
+    int32_t f, top_k, rows, upr;   // F, slots, rows per workgroup, pieces per row (F / 64)
+};
+
+template <int FMT>
+struct D1Raw;
+template <>
+struct D1Raw<kQ4_K> {
+    uint4 hdr, q0, q1;   // super-block header, the piece's 32 quant bytes
+};
+template <>
+struct D1Raw<kQ8_0> {
+    uint32_t v[17];      // two blocks, 68 bytes
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    float* lh = reinterpret_cast<float*>(lds);   // [top_k][F]
+    float* lpart = lh + a.top_k * a.f;          // one partial sum per unit
+    __shared__ int s_ex[kMaxTopK];
+    __shared__ float s_p[kMaxTopK];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+    const int per_slot = a.rows * a.upr;
+    const int total = a.top_k * per_slot;
+
+    // weights of this thread's units (loads first: they take longest)
+    D1Raw<FMT> raw[kD1Units];
+    bool live[kD1Units];
+#pragma unroll
+    for (int j = 0; j < kD1Units; ++j) {
+        const int u = tid + 256 * j;
+        const int slot = u / per_slot, rem = u % per_slot;
+        const int64_t row = r0 + rem / a.upr;
+        const int piece = rem % a.upr;
+        const int ex = u < total ? a.idx[slot] : -1;
+        live[j] = u < total && ex >= 0 && ex < a.e && row < a.hdim;
+        if (!live[j]) continue;
+        const uint8_t* rp = a.wd + ((int64_t)ex * a.hdim + row) * a.rb;
+        if constexpr (FMT == kQ4_K) {
+            const uint8_t* sb = rp + (int64_t)(piece / 4) * kQ4Bytes;
+            raw[j].hdr = load_once16(sb);
+            raw[j].q0 = load_once16(sb + 16 + 32 * (piece % 4));
+            raw[j].q1 = load_once16(sb + 32 + 32 * (piece % 4));
+        } else {
+            const uint32_t* q = reinterpret_cast<const uint32_t*>(rp + (int64_t)piece * 2 * kQ8Bytes);
+#pragma unroll
+            for (int i = 0; i < 17; ++i) raw[j].v[i] = __builtin_nontemporal_load(q + i);
+        }
+    }
+    // h of every slot (rows of slots without an expert are copied too and never
+    // used), the slots' experts and weights for the final sums
+    const int hq = a.top_k * a.f / 4;
+    for (int i = tid; i < hq; i += 256)
+        reinterpret_cast<float4*>(lh)[i] = reinterpret_cast<const float4*>(a.h)[i];
+    if (tid < a.top_k) {
+        s_ex[tid] = a.idx[tid];
+        s_p[tid] = a.probs[tid];
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int j = 0; j < kD1Units; ++j) {
+        const int u = tid + 256 * j;
+        if (u >= total) break;
+        float part = 0.f;
+        if (live[j]) {
+            const int slot = u / per_slot;
+            const int piece = (u % per_slot) % a.upr;
+            const float* hv = lh + slot * a.f + 64 * piece;
+            if constexpr (FMT == kQ4_K) {
+                // low nibbles: sub-block 2c, weights 64c + l; high: 2c + 1, 64c + 32 + l
+                const int c = piece % 4;
+                const Q4KScales sc = q4k_unpack(raw[j].hdr.y, raw[j].hdr.z, raw[j].hdr.w);
+                uint32_t sc0, m0, sc1, m1;
+                q4k_sub(sc, 2 * c, sc0, m0);
+                q4k_sub(sc, 2 * c + 1, sc1, m1);
+                const float d = half_bits_to_float(raw[j].hdr.x);
+                const float dmin = half_bits_to_float(raw[j].hdr.x >> 16);
+                const uint32_t qw[8] = {raw[j].q0.x, raw[j].q0.y, raw[j].q0.z, raw[j].q0.w,
+                                        raw[j].q1.x, raw[j].q1.y, raw[j].q1.z, raw[j].q1.w};
+                float dl = 0.f, dh = 0.f, sl = 0.f, sh = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 xl = reinterpret_cast<const float4*>(hv)[i];
+                    const float4 xh = reinterpret_cast<const float4*>(hv + 32)[i];
+                    const uint32_t lo = qw[i] & 0x0F0F0F0Fu, hi = (qw[i] >> 4) & 0x0F0F0F0Fu;
+                    dl += ubyte_f(lo, 0) * xl.x + ubyte_f(lo, 1) * xl.y + ubyte_f(lo, 2) * xl.z +
+                          ubyte_f(lo, 3) * xl.w;
+                    dh += ubyte_f(hi, 0) * xh.x + ubyte_f(hi, 1) * xh.y + ubyte_f(hi, 2) * xh.z +
+                          ubyte_f(hi, 3) * xh.w;
+                    sl += (xl.x + xl.y) + (xl.z + xl.w);
+                    sh += (xh.x + xh.y) + (xh.z + xh.w);
+                }
+                part = d * (float)sc0 * dl - dmin * (float)m0 * sl +
+                       (d * (float)sc1 * dh - dmin * (float)m1 * sh);
+            } else {
+                // block 0: scale bytes 0-1, quants 2-33; block 1: 34-35, 36-67
+                const uint32_t* v = raw[j].v;
+                float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 x0 = reinterpret_cast<const float4*>(hv)[i];
+                    const float4 x1 = reinterpret_cast<const float4*>(hv + 32)[i];
+                    const uint32_t q0 = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
+                    const uint32_t q1 = v[9 + i];
+                    d0 += sbyte_f(q0, 0) * x0.x + sbyte_f(q0, 1) * x0.y + sbyte_f(q0, 2) * x0.z +
+                          sbyte_f(q0, 3) * x0.w;
+                    d1 += sbyte_f(q1, 0) * x1.x + sbyte_f(q1, 1) * x1.y + sbyte_f(q1, 2) * x1.z +
+                          sbyte_f(q1, 3) * x1.w;
+                }
+                part = half_bits_to_float(v[0]) * d0 + half_bits_to_float(v[8] >> 16) * d1;
+            }
+        }
+        lpart[u] = part;
+    }
+    __syncthreads();
+
+    // each (slot, row): its pieces in order, into the h buffer (no longer read);
+    // then each row: the slots in order, weighted
+    for (int i = tid; i < a.top_k * a.rows; i += 256) {
+        const float* pp = lpart + (i / a.rows) * per_slot + (i % a.rows) * a.upr;
+        float dsum = 0.f;
+        for (int q = 0; q < a.upr; ++q) dsum += pp[q];
+        lh[i] = dsum;
+    }
+    __syncthreads();
+    if (tid < a.rows && r0 + tid < a.hdim) {
+        float acc = 0.f;
+        for (int s = 0; s < a.top_k; ++s) {
+            const int ex = s_ex[s];
+            if (ex >= 0 && ex < a.e) acc += s_p[s] * lh[s * a.rows + tid];
+        }
+        a.y[r0 + tid] = acc;
+    }
+}
+
 int moe_device_cus() {
     static int cus = 0;
     if (!cus) {
@@ -1234,7 +1392,8 @@ hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8
 template <int FMT, int NB>
 hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, int64_t e,
                           int64_t hdim, int64_t f, const float* x, int64_t t, int top_k,
-                          const int32_t* idx, const MoeWs& ws, hipStream_t s) {
+                          const int32_t* idx, const MoeWs& ws, hipStream_t s,
+                          bool down = true) {
     const int64_t p = t * top_k;
     const int64_t slots = p < e ? p : e;
     const bool inl = p <= kInlinePairs;
@@ -1256,7 +1415,7 @@ hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* w
     a.ldy = f;
     a.ws = ws;
     hipError_t err = launch_stage_rows<FMT, NB, 2>(a, slots, t, s);
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || !down) return err;
     MoeStage d{};
     d.idx = idx;
     d.p = (int32_t)p;
@@ -1355,6 +1514,43 @@ hipError_t launch_swiglu(int type, const uint8_t* wg, const uint8_t* wu, int64_t
     return q4 ? launch_mstage<kQ4_K, 2>(a, 1, s) : launch_mstage<kQ8_0, 2>(a, 1, s);
 }
 
+// The one-token down-and-combine kernel takes every (slot, row, piece) unit of
+// a workgroup's rows in one pass and keeps the h of all slots in LDS.
+static bool down1_fits(int64_t f, int top_k) {
+    return (int64_t)top_k * f * 4 + (int64_t)kD1Units * 256 * 4 <= 65536 &&
+           (int64_t)top_k * (f / 64) <= (int64_t)kD1Units * 256;
+}
+
+static hipError_t launch_down1(int type, const uint8_t* wd, int64_t e, int64_t hdim, int64_t f,
+                        const float* hbuf, const int32_t* idx, const float* probs, int top_k,
+                        float* y, hipStream_t s) {
+    Down1Args a;
+    a.wd = wd;
+    a.h = hbuf;
+    a.idx = idx;
+    a.probs = probs;
+    a.y = y;
+    a.e = e;
+    a.hdim = hdim;
+    a.rb = row_bytes(type, f);
+    a.f = (int32_t)f;
+    a.top_k = top_k;
+    a.upr = (int32_t)(f / 64);
+    // as many rows as the unit budget allows, but no more than it takes to
+    // give every compute unit two workgroups
+    const int64_t cap = (int64_t)kD1Units * 256 / ((int64_t)top_k * a.upr);
+    const int64_t wgs = 2 * (int64_t)moe_device_cus();
+    const int64_t spread = (hdim + wgs - 1) / wgs;
+    a.rows = (int32_t)std::max<int64_t>(1, std::min<int64_t>({cap, spread, 256}));
+    const size_t lds = ((size_t)top_k * f + (size_t)top_k * a.rows * a.upr) * 4;
+    const unsigned grid = (unsigned)((hdim + a.rows - 1) / a.rows);
+    if (type == kQ4_K)
+        hipLaunchKernelGGL(moe_down1_kernel<kQ4_K>, dim3(grid), dim3(256), lds, s, a);
+    else
+        hipLaunchKernelGGL(moe_down1_kernel<kQ8_0>, dim3(grid), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const float* dbuf, const int32_t* idx, const float* probs, int64_t e,
                           int64_t h, int64_t t, int top_k, float* y, hipStream_t s) {
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((h + 255) / 256), (unsigned)t), dim3(256), 0,
@@ -1385,6 +1581,13 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
     // One token: the vector-unit streaming stages.  Two or more: the matrix-core
     // stages (groups of up to 8 of an expert's tokens per pass).
     const bool q4 = type == kQ4_K;
+    if (t == 1 && down1_fits(f, top_k)) {
+        // one token: gate/up stage, then down and combine in one kernel
+        err = q4 ? launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s, false)
+                 : launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s, false);
+        if (err != hipSuccess) return err;
+        return launch_down1(type, wd, e, h, f, m.hbuf, idx, probs, top_k, y, s);
+    }
     if (t <= 1) err = q4 ? launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
                          : launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
     else err = q4 ? launch_experts_mfma<kQ4_K>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)

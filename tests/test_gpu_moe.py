@@ -208,10 +208,27 @@ def test_moe_repeated_expert_in_slots(g, fmt, t):
     check_bound(y, yref, bound, "moe repeated expert")
 
 
-def test_moe_reads_only_selected_experts(g):
+@pytest.mark.parametrize("fmt,t", [(Q4, 1), (Q8, 1), (Q4, 3)])
+def test_moe_out_of_range_slots(g, fmt, t):
+    """Slots naming no expert (negative or >= E) count with weight 0; the
+    oracle leaves them out."""
+    say(f"moe out-of-range slots fmt={fmt} t={t}")
+    e, h, f, k = 10, 512, 768, 5
+    mo = _small(8, fmt, e, h, f, t)
+    idx = np.array([[-1, 5, 10, 5, 99], [3, -7, 3, 1, 0], [9, 9, 12, 0, 4]][:t], dtype=np.int32)
+    probs = np.array([[0.3, 0.2, 0.25, 0.15, 0.1]] * t, dtype=np.float32)
+    y, _ = _run_moe(g, fmt, mo, idx, probs, e, h, f)
+    yref = oracle.moe(fmt, mo["wg"], mo["wu"], mo["wd"], e, h, f, mo["x"], idx,
+                      probs.astype(np.float64))
+    bound = _moe_bound(fmt, mo, mo["x"], idx, probs.astype(np.float64), e, h, f)
+    check_bound(y, yref, bound, "moe out-of-range slots")
+
+
+@pytest.mark.parametrize("t", [1, 3])
+def test_moe_reads_only_selected_experts(g, t):
     """NaN scales in every unselected expert leave the output unchanged."""
-    say("moe poison")
-    e, h, f, k, t = 12, 512, 256, 2, 3
+    say(f"moe poison t={t}")
+    e, h, f, k = 12, 512, 256, 2
     mo = _small(5, Q4, e, h, f, t)
     lref, _ = oracle.router_logits(mo["wr"], mo["x"])
     idx = oracle.topk(lref, k)
