@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (HBM counter calibration)")
-    p.add_argument("--only", choices=["q4k", "moe", "moe_prompt", "ffn", "gemm", "sweep"],
+    p.add_argument("--only", choices=["q4k", "moe", "moe_prompt", "ffn", "gemm", "sweep", "hbm"],
                    default=None,
                    help="run one secondary workload only (for profiling)")
     return p.parse_args()
@@ -290,6 +290,35 @@ def measured_traffic(kernel):
 def secondary(g, torch, synth, only=None):
     dev = torch.device("cuda:0")
     out = {}
+    if only in (None, "hbm"):
+        # What plain streams reach on this device, as a reference for the
+        # weight GB/s figures: a 1 GiB device copy (bytes read + written) and a
+        # library sum over 1 GiB (bytes read), 10 back-to-back eager calls each
+        # (the sum is kept out of graphs: it may record a memset node).
+        src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        acc = torch.empty((), dtype=torch.float32, device=dev)
+
+        def eager_ms(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        copy_ms = eager_ms(lambda: dst.copy_(src))
+        read_ms = eager_ms(lambda: torch.sum(src, dim=0, out=acc))
+        out["hbm_reference"] = {
+            "copy_GB/s": round(2 * src.nbytes / (copy_ms * 1e-3) / 1e9, 1),
+            "sum_read_GB/s": round(src.nbytes / (read_ms * 1e-3) / 1e9, 1),
+            "note": "torch device copy (read + write bytes) and torch.sum (read bytes), 1 GiB each",
+        }
+        del src, dst, acc
     if only in (None, "q4k"):
         res = {}
         for name, n, k in synth.Q4K_FFN_PAIR:
