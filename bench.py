@@ -88,7 +88,7 @@ def replay_ms(torch, graphs, reps, per_graph=1):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path would shard rows, experts or output columns across GPUs)",
               file=sys.stderr)
         sys.exit(2)
