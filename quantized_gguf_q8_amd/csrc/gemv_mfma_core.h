@@ -239,15 +239,19 @@ __device__ __forceinline__ void q4x4_to_f16(uint32_t v, f16x2 sc2, f16x2 msc2, u
     o1 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(b, sc2, msc2));
 }
 
-template <int FMT, int MT, int WM>
+// KCQ4: weights per chunk for Q4_K, 512 (two super-blocks) or 256; Q8_0 chunks
+// are 256 weights.
+template <int FMT, int MT, int WM, int KCQ4 = 512>
 struct MCfg {
+    static_assert(KCQ4 == 512 || KCQ4 == 256, "Q4_K chunk");
     static constexpr int WK = 4 / WM;
     static constexpr int RWG = 16 * WM;                         // rows per workgroup
-    static constexpr int KC = FMT == kQ8_0 ? 256 : 512;         // weights per chunk
-    static constexpr int CRB = FMT == kQ8_0 ? 272 : 288;        // bytes per row chunk
-    // LDS row stride: 68 dwords (Q8_0) / 76 dwords (Q4_K) put the 16 rows a wave
-    // reads at distinct multiples of 4 banks, so 64 lanes x 2 dwords spread evenly.
-    static constexpr int RS = FMT == kQ8_0 ? CRB : CRB + 16;
+    static constexpr int KC = FMT == kQ8_0 ? 256 : KCQ4;        // weights per chunk
+    static constexpr int CRB = FMT == kQ8_0 ? 272 : KC / 256 * 144;   // bytes per row chunk
+    // LDS row stride: 68 dwords (Q8_0) / 76 or 44 dwords (Q4_K) put the 16 rows a
+    // wave reads at distinct multiples of 4 banks, so 64 lanes x 2 dwords spread
+    // evenly.
+    static constexpr int RS = FMT == kQ8_0 ? CRB : CRB + (KC == 512 ? 16 : 32);
     static constexpr int NBLK = KC / 32;                        // 32-wide steps per chunk
     static constexpr int NSB = FMT == kQ4_K ? KC / 256 : 0;
     static constexpr int kW = RWG * RS;
@@ -266,10 +270,10 @@ struct MCfg {
 // activation fragments) into acc: Q8_0 per 32-weight block, Q4_K per
 // super-block with its min term.  k0 is the chunk's first column, kval the
 // matrix's K.
-template <int FMT, int MT, int WM>
+template <int FMT, int MT, int WM, int KCQ4 = 512>
 __device__ __forceinline__ void mfma_chunk(const uint8_t* lds, int k0, int kval, int lane, int wm,
                                            int wk, int j, int h, f32x4 (&acc)[MT]) {
-    using C = MCfg<FMT, MT, WM>;
+    using C = MCfg<FMT, MT, WM, KCQ4>;
     constexpr int WK = C::WK;
     const uint8_t* base = lds;
     const uint8_t* wrow = base + (16 * wm + j) * C::RS;
