@@ -1519,7 +1519,9 @@ hipError_t launch_swiglu(int type, const uint8_t* wg, const uint8_t* wu, int64_t
 // The one-token down-and-combine kernel takes every (slot, row, piece) unit of
 // a workgroup's rows in one pass and keeps the h of all slots in LDS.
 static bool down1_fits(int64_t f, int top_k) {
-    return (int64_t)top_k * f * 4 + (int64_t)kD1Units * 256 * 4 <= 65536 &&
+    // dynamic LDS (h of every slot, one partial per unit) plus the kernel's
+    // static slot arrays within the default 64 KiB
+    return ((int64_t)top_k * f + (int64_t)kD1Units * 256 + 2 * kMaxTopK) * 4 <= 65536 &&
            (int64_t)top_k * (f / 64) <= (int64_t)kD1Units * 256;
 }
 
