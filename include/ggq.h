@@ -31,8 +31,15 @@
  *  - Arguments are validated on the host before any HIP call; an invalid call
  *    returns a negative ggq_status and enqueues nothing.  A launch failure returns
  *    GGQ_ERR_LAUNCH.  Device faults surface at the caller's next synchronisation.
- *  - Results are deterministic: the same inputs give the same bits, and no
- *    floating-point atomics are used.
+ *  - Results are deterministic: the same inputs give the same bits.  The one
+ *    use of floating-point atomics is in the matrix-core decode GEMV (quant_gemv
+ *    and friends with a workspace, batch >= 2): a row tile whose K range is cut
+ *    in two adds both halves with atomic adds onto an output that an earlier
+ *    kernel of the same call zeroed.  0 + a + b gives the same bits in either
+ *    order, so the result does not depend on which half lands first; deeper K
+ *    cuts keep per-part sums in the workspace and add them in part order.
+ *  - Outputs never alias inputs or the workspace: y (or c, h) must not overlap
+ *    w, x (or a) or ws.
  *  - Nothing throws across this interface.
  */
 #ifndef GGQ_H
@@ -57,6 +64,9 @@ enum ggq_status {
     GGQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch */
 };
 
+/* Arithmetic of the prompt GEMM.  Only bf16 operands with fp32 accumulation are
+ * built; an int8 mode (per-32-column activation quantisation) would take the
+ * value 1 and is refused as GGQ_ERR_UNSUPPORTED. */
 enum ggq_gemm_mode { GGQ_GEMM_BF16 = 0 };
 
 /* Short English text for a status code; never NULL. */
@@ -202,7 +212,8 @@ int quant_gemm(int type, const void *w, int64_t n, int64_t k, const float *a, in
  *   x      device fp32 [T][H], 16-byte aligned
  *   idx    device int32 [T][top_k]
  *   probs  device fp32 [T][top_k]
- *   logits device fp32 [T][E], written (the selection is made on these values)
+ *   logits device fp32 [T][E], required (not NULL): always written, and the
+ *          selection is made on these stored values
  *   1 <= top_k <= min(E, 32), 1 <= E <= 1024, H % 4 == 0, H <= 2^24.
  *   T == 0 is a no-op.
  * Logits must be finite for the selection to be meaningful.
@@ -228,10 +239,13 @@ size_t moe_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f)
  * and down matrices are read once for all the tokens routed to it.
  * Stacked expert tensors: expert e of Wg/Wu (each F x H) starts at byte
  * e*F*(H/256)*144, expert e of Wd (H x F) at byte e*H*(F/256)*144.
- *   type   GGQ_Q4_K or GGQ_Q8_0; H and F multiples of 256; T*top_k <= 65536
+ *   type   GGQ_Q4_K or GGQ_Q8_0; H and F multiples of 256; T*top_k <= 65536;
+ *          T*H, T*top_k*F and T*top_k*H each below 2^30 (32-bit byte offsets)
  *   x      device fp32 [T][H];  y device fp32 [T][H]
- *   idx    device int32 [T][top_k], each in [0, E) (out-of-range entries get
- *          weight 0 and are never read out of bounds)
+ *   idx    device int32 [T][top_k], each in [0, E).  An out-of-range entry is
+ *          grouped with expert 0 (so expert 0's matrices may be read for it,
+ *          never anything out of bounds) and its term is left out of the sum,
+ *          whatever expert 0 holds.
  *   probs  device fp32 [T][top_k]
  *   ws     device workspace >= moe_workspace_size(E, T, top_k, H, F) bytes,
  *          256-byte aligned.  On return ws holds h at byte offset
@@ -269,8 +283,8 @@ size_t moe_gemm_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64
  * does not depend on the order in which pairs of one expert are processed, and
  * repeated calls give identical results.
  *   type, e, h, f, x, idx, probs, top_k, y   as for moe_expert_gemv
- *          (T*top_k <= 65536; out-of-range idx entries count as expert 0 with
- *          weight 0)
+ *          (T*top_k <= 65536; out-of-range idx entries are grouped with
+ *          expert 0 and their terms left out of the sum)
  *   ws     device workspace >= moe_gemm_workspace_size(E, T, top_k, H, F) bytes,
  *          256-byte aligned; its contents on entry do not matter
  * T == 0 is a no-op.  Errors: GGQ_ERR_ARG (also when a bf16 copy of x or h

@@ -259,6 +259,11 @@ int moe_expert_gemv(int type, const void* wg, const void* wu, const void* wd, in
                     void* stream) {
     const int rc = check_moe(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y);
     if (rc != GGQ_OK || t == 0) return rc;
+    // the stages address x [T][H], h [T*top_k][F] and the per-slot down
+    // outputs [T*top_k][H] with 32-bit buffer offsets
+    const int64_t lim = (int64_t)1 << 32;
+    if (t * h * 4 >= lim || t * top_k * f * 4 >= lim || t * top_k * h * 4 >= lim)
+        return GGQ_ERR_ARG;
     if (!ws || ws_bytes < ggq::moe_ws_bytes(e, t, top_k, h, f)) return GGQ_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
     return launched(ggq::launch_moe(type, static_cast<const uint8_t*>(wg),

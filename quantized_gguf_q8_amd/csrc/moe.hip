@@ -1025,8 +1025,10 @@ __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
     }
 }
 
-// y[t][r] = sum_s probs[t][s] * d[(t*top_k + s)][r], slot order; pairs whose
-// expert index is out of range contribute nothing.
+// y[t][r] = sum_s probs[t][s] * d[(t*top_k + s)][r], slot order.  Pairs whose
+// expert index is out of range were grouped with expert 0 and carry whatever
+// its matrices gave; their term is skipped (not multiplied by 0), so a
+// non-finite expert 0 cannot reach y through them.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ dbuf,
                                                       const int32_t* __restrict__ idx,
                                                       const float* __restrict__ probs,
@@ -1039,8 +1041,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int s = 0; s < top_k; ++s) {
         int64_t pi = ti * top_k + s;
         int32_t ex = idx[pi];
-        float p = (ex >= 0 && ex < e) ? probs[pi] : 0.f;
-        acc += p * dbuf[pi * hdim + r];
+        if (ex >= 0 && ex < e) acc += probs[pi] * dbuf[pi * hdim + r];
     }
     y[ti * hdim + r] = acc;
 }

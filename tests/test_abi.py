@@ -200,6 +200,9 @@ def test_moe_validation(g):
     assert call(x=B16 + 8) == ALIGN
     assert call(wsb=need - 1) == WS
     assert call(ws=D16 + 64) == ALIGN
+    # 32-bit buffer offsets: h [T*top_k][F] or x [T][H] past 4 GiB is refused
+    assert call(tt=8192, k=8, h=256, f=16384) == ARG
+    assert call(tt=65536, k=1, h=16384) == ARG
 
 
 def test_moe_gemm_validation(g):

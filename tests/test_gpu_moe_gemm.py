@@ -108,6 +108,25 @@ def test_moe_gemm_repeated_and_out_of_range(g, fmt):
     _check_tokens(fmt, mo, idx, probs, h, f, y, range(4), "moe gemm repeated")
 
 
+@pytest.mark.parametrize("fmt", [Q4, Q8])
+def test_moe_gemm_out_of_range_poisoned_expert0(g, fmt):
+    """Out-of-range slots are grouped with expert 0 yet contribute nothing:
+    with expert 0 unselected and its scales NaN, the output stays finite and
+    within the bound of the oracle, which leaves those slots out."""
+    say(f"moe gemm out of range, expert 0 poisoned fmt={fmt}")
+    e, h, f, k = 10, 512, 768, 5
+    mo = _small(10, fmt, e, h, f, 4)
+    idx = np.array([[4, 4, 7, 4, 1], [2, -2, 2, 2, 2], [9, 11, 9, 3, 5], [-1, 5, 10, 5, 99]],
+                   dtype=np.int32)
+    probs = np.array([[0.3, 0.2, 0.25, 0.15, 0.1]] * 4, dtype=np.float32)
+    blk = 144 if fmt == Q4 else 34
+    for key in ("wg", "wu", "wd"):
+        mo[key][0].reshape(-1, blk)[:, 0:2] = [0xFF, 0x7F]
+    y = _run(g, fmt, mo, idx, probs, e, h, f)
+    assert np.all(np.isfinite(y))
+    _check_tokens(fmt, mo, idx, probs, h, f, y, range(4), "moe gemm expert 0 poisoned")
+
+
 def test_moe_gemm_most_pairs(g):
     """T * top_k = 65536 pairs (the largest call), small matrices; sampled tokens."""
     say("moe gemm 65536 pairs")

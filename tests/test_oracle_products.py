@@ -101,6 +101,30 @@ def test_gemv_against_numpy_matmul(orc):
         assert np.all(np.abs(y - ref) <= 1e-13 * s)
 
 
+def test_matvec_f64_plain_and_magnitude_modes(orc):
+    """The fp64-input product used for the expert down projection and, with
+    absw, for the propagated MoE error bound (sum_c |w[r][c]| v[c]): both modes
+    against numpy matmuls of the exact weights and their magnitudes, with a
+    signed v so that a mode that forgets the |.| (or applies it to v) fails."""
+    n, k = 80, 1536
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal(k)
+    for fmt in (Q8, Q4):
+        w = synth.quant_matrix(fmt, n, k, seed=2, tensor_id=16)
+        wf = orc.dequant(fmt, w, n, k).astype(np.float64)
+        y, s = orc.matvec_f64(fmt, w, n, k, v)
+        assert np.all(np.abs(y - wf @ v) <= 1e-13 * s)
+        assert np.allclose(s, np.abs(wf) @ np.abs(v), rtol=1e-13, atol=0)
+        ya, sa = orc.matvec_f64(fmt, w, n, k, v, absw=True)
+        ref = np.abs(wf) @ v
+        assert np.all(np.abs(ya - ref) <= 1e-13 * sa)
+        assert np.allclose(sa, s, rtol=1e-13, atol=0)
+        # a non-negative v makes the magnitude product the sum of magnitudes
+        yp, sp = orc.matvec_f64(fmt, w, n, k, np.abs(v), absw=True)
+        assert np.allclose(yp, sp, rtol=1e-13, atol=0)
+        assert not np.allclose(ya, y)
+
+
 # --------------------------------------------------------------------------- #
 # Router / top-k / routing weights
 def test_topk_hand_built_ties(orc):
