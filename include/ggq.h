@@ -61,7 +61,8 @@ enum ggq_status {
     GGQ_ERR_UNSUPPORTED = -2, /* unknown format or mode */
     GGQ_ERR_ALIGN = -3,       /* a pointer or leading dimension breaks the alignment rules */
     GGQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the size query says */
-    GGQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch */
+    GGQ_ERR_LAUNCH = -5,      /* the HIP runtime refused a launch */
+    GGQ_ERR_SCRATCH = -6      /* quant_gemv_noalloc: the call needs more than its fixed scratch */
 };
 
 /* Arithmetic of the prompt GEMM.  Only bf16 operands with fp32 accumulation are
@@ -111,6 +112,32 @@ int quant_dequantize(int type, const void *w, int64_t n, int64_t k, float *out, 
  */
 int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t ldx,
                float *y, int64_t ldy, int batch, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * quant_gemv_noalloc -- quant_gemv for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same product, arguments and tolerance as quant_gemv
+ * with a workspace, but the workspace is a fixed array of
+ * GGQ_NOALLOC_SCRATCH_BYTES in device memory that the library holds on each GPU
+ * it runs on until the process ends.  The call allocates and frees nothing.
+ *   batch 1 runs on the vector units and uses no scratch.  batch >= 2 runs on
+ *   the matrix cores with the activation fragments in the scratch, and also
+ *   cuts K across workgroups when the partial-sum planes
+ *   (quant_gemv_split_workspace_size) fit; with the same workspace size
+ *   quant_gemv gives the same bits.
+ * Calls on one GPU share its scratch, and each call leaves its contents behind
+ * (the kernels clear what must start at zero): calls that can overlap on one
+ * GPU (several streams or host threads) race and must be serialised by the
+ * caller.  The stream must belong to the current device; the scratch address
+ * of a device is looked up on the first call made with that device current.
+ * Errors: as quant_gemv, and GGQ_ERR_SCRATCH when
+ * quant_gemv_workspace_size(type, K, batch) exceeds the scratch (nothing is
+ * launched); GGQ_ERR_LAUNCH if the scratch address cannot be obtained.
+ */
+#define GGQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int quant_gemv_noalloc(int type, const void *w, int64_t n, int64_t k, const float *x,
+                       int64_t ldx, float *y, int64_t ldy, int batch, void *stream);
 
 /* Workspace bytes one matrix of K columns needs in quant_gemv (and in each
  * descriptor of quant_gemv_grouped) at this batch; 0 on bad arguments. */

@@ -44,6 +44,7 @@ _SIGS = {
     "ggq_version": (_I, []),
     "quant_dequantize": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "quant_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _P, _SZ, _P]),
+    "quant_gemv_noalloc": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _P]),
     "quant_gemv_workspace_size": (_SZ, [_I, _I64, _I]),
     "quant_gemv_split_workspace_size": (_SZ, [_I, _I64, _I64, _I]),
     "quant_gemv_grouped": (_I, [_I, _P, _I, _I, _P, _SZ, _P]),
@@ -169,6 +170,26 @@ def quant_gemv(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
     _ck("quant_gemv", _lib.quant_gemv(fmt, _ptr(w), n, k, _ptr(x2), k, _ptr(y), n, b, _ptr(wst),
                                       0 if wst is None else wst.numel(), _stream()))
     return y[0] if squeeze else y
+
+
+def quant_gemv_noalloc(fmt: int, w: torch.Tensor, n: int, k: int, x: torch.Tensor,
+                       y: torch.Tensor) -> torch.Tensor:
+    """quant_gemv with the library's fixed device scratch as its workspace: no
+    device allocation in the call (y must be given).  Calls on one GPU share
+    the scratch; overlapping calls race."""
+    _wbytes(w, fmt, n, k)
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    _dev(x2, "x", torch.float32)
+    if x2.shape[1] != k:
+        raise ValueError(f"x has {x2.shape[1]} columns, K = {k}")
+    b = x2.shape[0]
+    _dev(y, "y", torch.float32)
+    if y.numel() < b * n:
+        raise ValueError(f"y holds {y.numel()} floats, {b * n} needed")
+    _ck("quant_gemv_noalloc", _lib.quant_gemv_noalloc(fmt, _ptr(w), n, k, _ptr(x2), k, _ptr(y),
+                                                      n, b, _stream()))
+    return y
 
 
 def quant_gemv_swiglu(fmt: int, wg: torch.Tensor, wu: torch.Tensor, n: int, k: int,

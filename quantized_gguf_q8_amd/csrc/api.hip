@@ -3,6 +3,8 @@
 // HIP call, so a rejected call enqueues nothing.
 #include <limits.h>
 
+#include <mutex>
+
 #include "ggq.h"
 #include "ggq_launch.h"
 
@@ -32,6 +34,8 @@ const char* ggq_status_string(int status) {
         case GGQ_ERR_ALIGN: return "misaligned pointer or leading dimension";
         case GGQ_ERR_WORKSPACE: return "workspace missing or too small";
         case GGQ_ERR_LAUNCH: return "kernel launch failed";
+        case GGQ_ERR_SCRATCH:
+            return "call needs more than the fixed scratch of the no-allocation entry point";
         default: return "unknown status";
     }
 }
@@ -114,6 +118,57 @@ int quant_gemv(int type, const void* w, int64_t n, int64_t k, const float* x, in
     const int st = check_gemv(type, d, batch);
     if (st != GGQ_OK || n == 0) return st;
     return run_gemv(type, &d, 1, batch, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// quant_gemv_noalloc: quant_gemv whose matrix-core workspace is a fixed array
+// in device memory, for callers that cannot allocate.  Each device holds its
+// own copy of `scratch` (allocated when the code object loads, kept until the
+// process ends).  Host code never uses the array's name as an address: the
+// device address is looked up once per device and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[GGQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device.
+int scratch_of_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GGQ_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GGQ_ERR_LAUNCH;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return GGQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int quant_gemv_noalloc(int type, const void* w, int64_t n, int64_t k, const float* x,
+                       int64_t ldx, float* y, int64_t ldy, int batch, void* stream) {
+    const ggq_gemv_desc d{w, n, k, x, ldx, y, ldy};
+    const int st = check_gemv(type, d, batch);
+    if (st != GGQ_OK || n == 0) return st;
+    // batch 1 (and Q8_0 rows that are not whole 256-column chunks) run on the
+    // vector units, which use no workspace
+    if (!mfma_ok(type, &d, 1, batch)) return run_gemv(type, &d, 1, batch, nullptr, 0, stream);
+    const size_t need = gemv_ws_need(type, &d, 1, batch);
+    if (need > (size_t)GGQ_NOALLOC_SCRATCH_BYTES) return GGQ_ERR_SCRATCH;
+    void* sp = nullptr;
+    const int rc = scratch_of_current_device(&sp);
+    if (rc != GGQ_OK) return rc;
+    // K parts (partial sums in the workspace) when their planes fit as well
+    const size_t split = gemv_split_need(type, &d, 1, batch);
+    return run_gemv(type, &d, 1, batch, sp,
+                    split <= (size_t)GGQ_NOALLOC_SCRATCH_BYTES ? split : need, stream);
 }
 
 size_t quant_gemv_workspace_size(int type, int64_t k, int batch) {

@@ -180,6 +180,21 @@ def test_route_validation(g):
     assert L.moe_route(None, 128, 2048, None, 0, 8, None, None, None, None) == OK
 
 
+def test_noalloc_validation(g):
+    L = g._lib
+    # argument checks are those of quant_gemv, before any device work
+    assert L.quant_gemv_noalloc(99, A16, 4, 32, B16, 32, C16, 4, 2, None) == UNSUP
+    assert L.quant_gemv_noalloc(8, A16, 4, 33, B16, 33, C16, 4, 2, None) == ARG
+    assert L.quant_gemv_noalloc(8, A16, 4, 256, B16, 256, C16, 4, 17, None) == ARG
+    assert L.quant_gemv_noalloc(8, A16, 4, 256, B16 + 8, 256, C16, 4, 2, None) == ALIGN
+    assert L.quant_gemv_noalloc(8, A16, 0, 256, B16, 256, C16, 0, 2, None) == OK   # N = 0
+    # more activation fragments than the fixed scratch holds: refused, nothing launched
+    k = 1 << 19
+    assert L.quant_gemv_workspace_size(8, k, 16) > (16 << 20)
+    assert L.quant_gemv_noalloc(8, A16, 1, k, B16, k, C16, 1, 16, None) == -6
+    assert b"scratch" in L.ggq_status_string(-6)
+
+
 def test_moe_validation(g):
     L = g._lib
     need = L.moe_workspace_size(128, 16, 8, 2048, 768)
