@@ -440,7 +440,7 @@ def secondary(g, torch, synth, only=None):
             hh = torch.empty((b, n), dtype=torch.float32, device=dev)
             yg = torch.empty((b, n), dtype=torch.float32, device=dev)
             yu = torch.empty((b, n), dtype=torch.float32, device=dev)
-            ws = None if b == 1 else torch.empty(g.quant_gemv_workspace_size(g.Q8_0, k, b),
+            ws = None if b == 1 else torch.zeros(g.quant_gemv_workspace_size(g.Q8_0, k, b),
                                                  dtype=torch.uint8, device=dev)
             graphs = capture(torch, [lambda: [g.quant_gemv_swiglu(g.Q8_0, a_, u_, n, k, x, hh, ws)
                                               for a_, u_ in cps]])
@@ -480,7 +480,7 @@ def secondary(g, torch, synth, only=None):
                 row["gemv_us"] = round(ms * 1e3, 2)
                 row["gemv_GB/s"] = round(wh.nbytes / (ms * 1e-3) / 1e9, 1)
                 del graphs, calls
-            wsg = torch.empty(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
+            wsg = torch.zeros(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
                               device=dev)
             graphs = capture(torch, [lambda: [g.quant_gemm(fmt, cw, n, k, a, c, wsg)
                                               for cw in cps]])
@@ -502,7 +502,7 @@ def secondary(g, torch, synth, only=None):
             w = torch.from_numpy(synth.quant_matrix(fmt, n, k, seed=0, tensor_id=tid)).to(dev)
             a = torch.from_numpy(synth.normal_f32((m, k), 0, tid + 1)).to(dev)
             c = torch.empty((m, n), dtype=torch.float32, device=dev)
-            ws = torch.empty(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
+            ws = torch.zeros(g.quant_gemm_workspace_size(fmt, m, n, k), dtype=torch.uint8,
                              device=dev)
             per = 4   # calls per graph
             graphs = capture(torch, [lambda: [g.quant_gemm(fmt, w, n, k, a, c, ws)

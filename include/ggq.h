@@ -40,6 +40,14 @@
  *    cuts keep per-part sums in the workspace and add them in part order.
  *  - Outputs never alias inputs or the workspace: y (or c, h) must not overlap
  *    w, x (or a) or ws.
+ *  - Workspaces of quant_gemv, quant_gemv_grouped, quant_gemv_swiglu and
+ *    quant_gemm begin with a control block of GGQ_CTRL_BYTES: per-row-tile
+ *    counters through which the workgroups of a single-launch GEMV learn which
+ *    of them adds up a tile's K parts.  It must be zero before a workspace is
+ *    first used (allocate it zeroed, or clear those bytes once); every call
+ *    leaves it zero, and the rest of the workspace may hold anything.  These
+ *    calls can therefore share one workspace; a workspace that served other
+ *    calls (moe_*) or a call that failed on the device must be cleared again.
  *  - Nothing throws across this interface.
  */
 #ifndef GGQ_H
@@ -51,6 +59,8 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+#define GGQ_CTRL_BYTES 4096u
 
 /* Block formats, numbered as GGUF tensor types. */
 enum ggq_type { GGQ_Q8_0 = 8, GGQ_Q4_K = 12 };
@@ -99,11 +109,15 @@ int quant_dequantize(int type, const void *w, int64_t n, int64_t k, float *out, 
  *   y     device fp32 [batch][ldy], ldy >= N
  *   batch 1..16
  *   ws    NULL, or device workspace of at least quant_gemv_workspace_size(type, K,
- *         batch) bytes, 256-byte aligned, not shared with a call running at the
- *         same time.  With a workspace and batch >= 2 the activations are split
- *         into exact fp16 pairs once and the products run on the matrix cores
- *         (fp32 accumulation); with NULL every batch row costs one fp32 FMA per
- *         weight on the vector units.  Both meet the same tolerance.
+ *         batch) bytes, 256-byte aligned, control block zero (see above), not
+ *         shared with a call running at the same time.  With a workspace the
+ *         activations are split into exact fp16 pairs and the products run on
+ *         the matrix cores (fp32 accumulation): for one matrix, when the
+ *         workspace also holds the K-part sums (quant_gemv_split_workspace_size),
+ *         in a single launch that splits the activations itself; otherwise
+ *         (batch >= 2) after a pass that splits them.  With NULL every batch row
+ *         costs one fp32 FMA per weight on the vector units.  All paths meet the
+ *         same tolerance.
  * A matrix may hold at most 4 GiB ((N + 64) * row bytes < 2^32) and an activation
  * block batch * ldx * 4 < 2^32 bytes.
  * N == 0 is a no-op.  Errors: GGQ_ERR_ARG (null, K not a multiple of the block,
@@ -125,10 +139,11 @@ int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, in
  *   cuts K across workgroups when the partial-sum planes
  *   (quant_gemv_split_workspace_size) fit; with the same workspace size
  *   quant_gemv gives the same bits.
- * Calls on one GPU share its scratch, and each call leaves its contents behind
- * (the kernels clear what must start at zero): calls that can overlap on one
- * GPU (several streams or host threads) race and must be serialised by the
- * caller.  The stream must belong to the current device; the scratch address
+ * Calls on one GPU share its scratch, and each call leaves its contents behind:
+ * the scratch starts zeroed when the library loads and every call leaves its
+ * control block zero (the rest is rewritten by each call before use).  Calls
+ * that can overlap on one GPU (several streams or host threads) race and must
+ * be serialised by the caller.  The stream must belong to the current device; the scratch address
  * of a device is looked up on the first call made with that device current.
  * Errors: as quant_gemv, and GGQ_ERR_SCRATCH when
  * quant_gemv_workspace_size(type, K, batch) exceeds the scratch (nothing is
@@ -139,18 +154,19 @@ int quant_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, in
 int quant_gemv_noalloc(int type, const void *w, int64_t n, int64_t k, const float *x,
                        int64_t ldx, float *y, int64_t ldy, int batch, void *stream);
 
-/* Workspace bytes one matrix of K columns needs in quant_gemv (and in each
- * descriptor of quant_gemv_grouped) at this batch; 0 on bad arguments. */
+/* Workspace bytes one matrix of K columns needs in quant_gemv at this batch
+ * (control block included); 0 on bad arguments. */
 size_t quant_gemv_workspace_size(int type, int64_t k, int batch);
 
 /* Larger workspace for a matrix of N rows and K columns: with at least this
  * many bytes (summed over the descriptors of a grouped call) the matrix-core
- * path may also cut each row tile into up to 16 K parts, run them on separate
- * workgroups, keep their fp32 partial sums in the workspace and add them in
- * part order in a second launch -- for short, long-K matrices, whose row tiles
- * alone leave most of the chip idle.  The result is as deterministic and
- * within the same tolerance as without.  With less (but at least
- * quant_gemv_workspace_size) nothing changes.  0 on bad arguments. */
+ * path may also cut each row tile into K parts, run them on separate
+ * workgroups and keep their fp32 partial sums in the workspace, added in part
+ * order (by the last workgroup of the tile, or by a second launch) -- for
+ * short, long-K matrices, whose row tiles alone leave most of the chip idle.
+ * The result is as deterministic and within the same tolerance as without.
+ * With less (but at least quant_gemv_workspace_size) nothing changes.  0 on
+ * bad arguments. */
 size_t quant_gemv_split_workspace_size(int type, int64_t n, int64_t k, int batch);
 
 /*
@@ -162,8 +178,10 @@ size_t quant_gemv_split_workspace_size(int type, int64_t n, int64_t k, int batch
  * share one launch instead of each paying its own start-up.  The descriptor
  * array is read on the host during the call and may be reused afterwards.
  *   count  1..16;  descriptors with n == 0 are skipped
- *   ws     NULL, or at least the sum over descriptors of
- *          quant_gemv_workspace_size(type, descs[i].k, batch) bytes
+ *   ws     NULL, or at least GGQ_CTRL_BYTES plus, per descriptor,
+ *          quant_gemv_workspace_size(type, descs[i].k, batch) - GGQ_CTRL_BYTES
+ *          bytes (the plain sum of quant_gemv_workspace_size always suffices);
+ *          control block zero
  * Errors: as quant_gemv, for any descriptor; nothing is launched on error.
  */
 typedef struct ggq_gemv_desc {
@@ -194,8 +212,9 @@ int quant_gemv_grouped(int type, const ggq_gemv_desc *descs, int count, int batc
  *   h       device fp32 [batch][ldh], ldh >= N
  *   batch   1..16
  *   ws      batch >= 2: device workspace of at least
- *           quant_gemv_workspace_size(type, K, batch) bytes, 256-byte aligned
- *           (the activation fragments); batch 1: may be NULL
+ *           quant_gemv_workspace_size(type, K, batch) bytes, 256-byte aligned,
+ *           control block zero (the activation fragments follow it); batch 1:
+ *           may be NULL
  * N == 0 is a no-op.  Errors: as quant_gemv; GGQ_ERR_ARG for K % 256 != 0;
  * GGQ_ERR_WORKSPACE for batch >= 2 without the workspace.
  */
@@ -221,7 +240,7 @@ size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int 
  *   c     device fp32 [M][ldc], ldc >= N
  *   mode  GGQ_GEMM_BF16
  *   ws    device workspace of at least quant_gemm_workspace_size() bytes,
- *         256-byte aligned; its contents on entry do not matter
+ *         256-byte aligned, control block zero; the rest may hold anything
  * M == 0 or N == 0 is a no-op.  Errors: GGQ_ERR_ARG, GGQ_ERR_ALIGN,
  * GGQ_ERR_WORKSPACE, GGQ_ERR_UNSUPPORTED.
  */

@@ -22,6 +22,9 @@ import torch
 Q8_0 = 8
 Q4_K = 12
 GEMM_BF16 = 0
+# Bytes at the start of every quant_gemv / quant_gemm workspace that must be zero
+# before its first use (every call leaves them zero).
+CTRL_BYTES = 4096
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libggq.so")
@@ -136,14 +139,15 @@ def quant_gemv_split_workspace_size(fmt: int, n: int, k: int, batch: int) -> int
 
 
 def _ws_arg(ws, need, device):
-    """None -> no workspace (vector-unit path); "auto" -> allocate `need` bytes;
-    else a uint8 tensor."""
+    """None -> no workspace (vector-unit path); "auto" -> allocate `need` bytes,
+    zeroed (the workspace's control block must start at zero); else a uint8
+    tensor whose first CTRL_BYTES are zero before its first use."""
     if ws is None:
         return None
     if isinstance(ws, str):
         if ws != "auto":
             raise ValueError("ws must be None, 'auto' or a uint8 device tensor")
-        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        return torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
     _dev(ws, "ws", torch.uint8)
     return ws
 
@@ -288,7 +292,7 @@ def quant_gemm(fmt: int, w: torch.Tensor, n: int, k: int, a: torch.Tensor,
     _dev(c, "c", torch.float32)
     need = quant_gemm_workspace_size(fmt, m, n, k, mode)
     if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=w.device)
     _dev(ws, "ws", torch.uint8)
     _ck("quant_gemm", _lib.quant_gemm(fmt, _ptr(w), n, k, _ptr(a), k, m, _ptr(c), n, mode,
                                       _ptr(ws), ws.numel(), _stream()))

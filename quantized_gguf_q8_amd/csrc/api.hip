@@ -85,17 +85,22 @@ static bool mfma_ok(int type, const ggq_gemv_desc* d, int count, int batch) {
     return true;
 }
 
+// Workspace bytes (control block included) of the staged matrix-core path.
 static size_t gemv_ws_need(int type, const ggq_gemv_desc* d, int count, int batch) {
-    size_t need = 0;
+    size_t need = ggq::kCtrlBytes;
     for (int i = 0; i < count; ++i)
         if (d[i].n > 0) need += ggq::gemv_mfma_ws_bytes(type, d[i].k, batch);
     return need;
 }
 
 static size_t gemv_split_need(int type, const ggq_gemv_desc* d, int count, int batch) {
-    size_t need = 0;
+    size_t need = ggq::kCtrlBytes;
     for (int i = 0; i < count; ++i)
         if (d[i].n > 0) need += ggq::gemv_split_ws_bytes(type, d[i].n, d[i].k, batch);
+    if (count == 1 && d[0].n > 0) {
+        const size_t ks = ggq::gemv_ks_ws_bytes(type, d[0].n, d[0].k, batch);
+        need = ks > need ? ks : need;
+    }
     return need;
 }
 
@@ -104,10 +109,17 @@ static int run_gemv(int type, const ggq_gemv_desc* d, int count, int batch, void
     if (ws) {
         if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
         if (ws_bytes < gemv_ws_need(type, d, count, batch)) return GGQ_ERR_WORKSPACE;
+        // one matrix, batch >= 2: a single launch with the activation split done
+        // in-kernel (at batch 1 the vector units' streaming kernel is faster)
+        ggq::GemvKsPlan plan;
+        if (count == 1 && batch >= 2 &&
+            ggq::gemv_ks_plan(type, d[0].n, d[0].k, batch, ws_bytes, plan))
+            return launched(ggq::launch_gemv_ks(type, d[0], batch, plan, ws, as_stream(stream)));
         const bool parts = ws_bytes >= gemv_split_need(type, d, count, batch);
         if (mfma_ok(type, d, count, batch))
-            return launched(
-                ggq::launch_gemv_mfma(type, d, count, batch, ws, parts, as_stream(stream)));
+            return launched(ggq::launch_gemv_mfma(type, d, count, batch,
+                                                  static_cast<uint8_t*>(ws) + ggq::kCtrlBytes,
+                                                  parts, as_stream(stream)));
     }
     return launched(ggq::launch_gemv_group(type, d, count, batch, as_stream(stream)));
 }
@@ -174,13 +186,15 @@ int quant_gemv_noalloc(int type, const void* w, int64_t n, int64_t k, const floa
 size_t quant_gemv_workspace_size(int type, int64_t k, int batch) {
     const int blk = block_of(type);
     if (!blk || k <= 0 || k % blk != 0 || batch < 1 || batch > kMaxBatch) return 0;
-    return ggq::gemv_mfma_ws_bytes(type, k, batch);
+    return ggq::kCtrlBytes + ggq::gemv_mfma_ws_bytes(type, k, batch);
 }
 
 size_t quant_gemv_split_workspace_size(int type, int64_t n, int64_t k, int batch) {
     const size_t base = quant_gemv_workspace_size(type, k, batch);
     if (!base || n < 0 || n > INT_MAX) return 0;
-    return ggq::gemv_split_ws_bytes(type, n, k, batch);
+    const size_t old = ggq::kCtrlBytes + ggq::gemv_split_ws_bytes(type, n, k, batch);
+    const size_t ks = n > 0 ? ggq::gemv_ks_ws_bytes(type, n, k, batch) : 0;
+    return ks > old ? ks : old;
 }
 
 int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batch, void* ws,
@@ -203,9 +217,10 @@ int quant_gemv_grouped(int type, const ggq_gemv_desc* descs, int count, int batc
 constexpr int64_t kGemmViaGemvRows = 16;
 
 static size_t gemm_ws_need(int type, int64_t m, int64_t n, int64_t k) {
-    size_t need = ggq::gemm_workspace_bytes(type, m, n, k);
+    size_t need = ggq::kCtrlBytes + ggq::gemm_workspace_bytes(type, m, n, k);
     if (m >= 1 && m <= kGemmViaGemvRows) {
-        const size_t g = ggq::gemv_split_ws_bytes(type, n, k, (int)m);
+        const ggq_gemv_desc d{nullptr, n, k, nullptr, k, nullptr, n};
+        const size_t g = gemv_split_need(type, &d, 1, (int)m);
         need = g > need ? g : need;
     }
     return need;
@@ -222,8 +237,10 @@ int quant_gemv_swiglu(int type, const void* wg, const void* wu, int64_t n, int64
     if (k % 256 != 0) return GGQ_ERR_ARG;
     if (n == 0) return GGQ_OK;
     if (batch >= 2) {
-        if (!ws || ws_bytes < ggq::gemv_mfma_ws_bytes(type, k, batch)) return GGQ_ERR_WORKSPACE;
+        if (!ws || ws_bytes < ggq::kCtrlBytes + ggq::gemv_mfma_ws_bytes(type, k, batch))
+            return GGQ_ERR_WORKSPACE;
         if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+        ws = static_cast<uint8_t*>(ws) + ggq::kCtrlBytes;
     }
     return launched(ggq::launch_swiglu(type, static_cast<const uint8_t*>(wg),
                                        static_cast<const uint8_t*>(wu), n, k, x, ldx, h, ldh,
@@ -259,7 +276,8 @@ int quant_gemm(int type, const void* w, int64_t n, int64_t k, const float* a, in
             return run_gemv(type, &d, 1, (int)m, ws, ws_bytes, stream);
     }
     return launched(ggq::launch_gemm(type, static_cast<const uint8_t*>(w), n, k, a, lda, m, c, ldc,
-                                     ws, as_stream(stream)));
+                                     static_cast<uint8_t*>(ws) + ggq::kCtrlBytes,
+                                     as_stream(stream)));
 }
 
 int moe_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t, int top_k,

@@ -12,6 +12,12 @@ namespace ggq {
 
 using GemvDesc = ggq_gemv_desc;
 
+// Every quant_gemv / quant_gemm workspace begins with a control block: the
+// per-row-tile counters of the single-launch GEMV (gemv_ks.hip).  It must be
+// zero before a workspace is first used; every call leaves it zero.  The other
+// layouts start after it, so one workspace can serve all of these calls.
+constexpr size_t kCtrlBytes = 4096;
+
 int64_t row_bytes(int type, int64_t k);
 
 hipError_t launch_dequant(int type, const uint8_t* w, int64_t n, int64_t k, float* out,
@@ -27,6 +33,17 @@ hipError_t launch_gemv_mfma(int type, const GemvDesc* descs, int count, int batc
 hipError_t launch_gemv_group(int type, const GemvDesc* descs, int count, int batch, hipStream_t s);
 hipError_t launch_gemv(int type, const uint8_t* w, int64_t n, int64_t k, const float* x,
                        int64_t ldx, float* y, int64_t ldy, int batch, hipStream_t s);
+
+// One-launch matrix-core GEMV for a single matrix (gemv_ks.hip): the plan, or
+// false when the shape or the workspace does not suit it.
+struct GemvKsPlan {
+    int t, mt, tiles, parts;
+    size_t ws_bytes;   // workspace the plan needs (0 without K parts)
+};
+bool gemv_ks_plan(int type, int64_t n, int64_t k, int batch, size_t ws_bytes, GemvKsPlan& p);
+size_t gemv_ks_ws_bytes(int type, int64_t n, int64_t k, int batch);
+hipError_t launch_gemv_ks(int type, const GemvDesc& d, int batch, const GemvKsPlan& p, void* ws,
+                          hipStream_t s);
 
 // Workspace layout of the prompt GEMM.
 size_t gemm_workspace_bytes(int type, int64_t m, int64_t n, int64_t k);

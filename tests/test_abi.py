@@ -122,7 +122,9 @@ def test_gemv_grouped_validation(g):
     arr[1] = g.GemvDesc(A16 + 4, 4, 2048, B16, 2048, C16, 4)   # misaligned member
     assert L.quant_gemv_grouped(8, p, 3, 1, None, 0, None) == ALIGN
     arr[1] = g.GemvDesc(A16, 4, 2048, B16, 2048, C16, 4)
-    need = 3 * L.quant_gemv_workspace_size(8, 2048, 4)
+    # one control block, then each member's activation fragments
+    one = L.quant_gemv_workspace_size(8, 2048, 4)
+    need = g.CTRL_BYTES + 3 * (one - g.CTRL_BYTES)
     assert L.quant_gemv_grouped(8, p, 3, 4, D16, need - 1, None) == WS
     for i in range(3):
         arr[i] = g.GemvDesc(None, 0, 2048, None, 2048, None, 0)  # all empty: no-op

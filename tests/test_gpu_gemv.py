@@ -136,8 +136,8 @@ def test_gemv_split_workspace(g, fmt, n, k, b):
     x = synth.normal_f32((b, k), seed=9, tensor_id=n + k + 1)
     wd, xd = dev(w), dev(x)
     yr, s = oracle.gemv(fmt, w, n, k, x)
-    small = torch.empty(g.quant_gemv_workspace_size(fmt, k, b), dtype=torch.uint8, device="cuda")
-    big = torch.empty(g.quant_gemv_split_workspace_size(fmt, n, k, b), dtype=torch.uint8,
+    small = torch.zeros(g.quant_gemv_workspace_size(fmt, k, b), dtype=torch.uint8, device="cuda")
+    big = torch.zeros(g.quant_gemv_split_workspace_size(fmt, n, k, b), dtype=torch.uint8,
                       device="cuda")
     y1 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=small))
     y2 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=big))
@@ -145,6 +145,53 @@ def test_gemv_split_workspace(g, fmt, n, k, b):
     check_rel(y1, yr, s, GEMV_TOL, "minimal workspace")
     check_rel(y2, yr, s, GEMV_TOL, "split workspace")
     assert np.array_equal(y2, y3)
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [
+    (Q4, 2560, 9728, 16), (Q4, 9728, 2560, 4), (Q8, 1024, 1024, 1), (Q8, 300, 6144, 9),
+    (Q4, 33, 20480, 2),      # 20 K parts on 3 row tiles, ragged last tile
+])
+def test_gemv_single_launch_workspace_and_graph_replays(g, fmt, n, k, b):
+    """The one-launch matrix-core GEMV of a single matrix: its K parts are added
+    in part order by the workgroup that finishes a row tile last, counted in the
+    workspace's control block.  A workspace whose control block is zero and
+    whose rest is random bytes must not matter, every call must leave the
+    control block zero, and replays of a captured call must give the eager bits
+    each time."""
+    say(f"gemv single launch fmt={fmt} n={n} k={k} b={b}")
+    w = synth.quant_matrix(fmt, n, k, seed=12, tensor_id=n + 3 * k)
+    x = synth.normal_f32((b, k), seed=12, tensor_id=n + 3 * k + 1)
+    wd, xd = dev(w), dev(x)
+    yr, s = oracle.gemv(fmt, w, n, k, x)
+    nbytes = g.quant_gemv_split_workspace_size(fmt, n, k, b)
+    rng = np.random.default_rng(5)
+    raw = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+    raw[:g.CTRL_BYTES] = 0
+    ws = dev(raw)
+    y0 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=ws))
+    check_rel(y0, yr, s, GEMV_TOL, "garbage workspace")
+    assert not host(ws[:g.CTRL_BYTES]).any(), "control block left non-zero"
+    y1 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=ws))
+    assert np.array_equal(y0, y1)
+    yg = torch.full((b, n), float("nan"), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.quant_gemv(fmt, wd, n, k, xd, y=yg, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.quant_gemv(fmt, wd, n, k, xd, y=yg, ws=ws)
+    for rep in range(4):
+        yg.fill_(float("nan"))
+        graph.replay()
+        got = host(yg)
+        assert np.array_equal(got, y0), f"replay {rep}"
+        # eager work between replays, on the same workspace
+        y2 = host(g.quant_gemv(fmt, wd, n, k, xd, ws=ws))
+        assert np.array_equal(y2, y0)
+    assert not host(ws[:g.CTRL_BYTES]).any(), "control block left non-zero"
 
 
 # --------------------------------------------------------------------------- #
@@ -185,7 +232,7 @@ def test_gemv_swiglu_strided_and_repeatable(g):
         xp = torch.zeros((b, ldx), dtype=torch.float32, device="cuda")
         xp[:, :k] = dev(x)
         hp = torch.full((b, ldh), 7.0, dtype=torch.float32, device="cuda")
-        ws = torch.empty(max(g.quant_gemv_workspace_size(fmt, k, b), 256), dtype=torch.uint8,
+        ws = torch.zeros(max(g.quant_gemv_workspace_size(fmt, k, b), 256), dtype=torch.uint8,
                          device="cuda")
         wgd, wud = dev(wg), dev(wu)
         def call():
@@ -328,7 +375,7 @@ def test_graph_replays_match_eager(g):
     wq = dev(synth.q4_k_matrix(256, 1024, seed=1, tensor_id=5))
     a = dev(synth.normal_f32((64, 1024), seed=1, tensor_id=6))
     c = torch.empty((64, 256), device="cuda")
-    ws = torch.empty(g.quant_gemm_workspace_size(Q4, 64, 256, 1024), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(g.quant_gemm_workspace_size(Q4, 64, 256, 1024), dtype=torch.uint8, device="cuda")
     mo = synth.moe_layer(seed=2, n_tokens=4)
     wr, x = dev(mo["wr"]), dev(mo["x"])
     wg, wu, wd = dev(mo["wg"]), dev(mo["wu"]), dev(mo["wd"])

@@ -39,7 +39,7 @@ def _call_noalloc(g, fmt, w, n, k, x):
 def _call_ws(g, fmt, w, n, k, x, ws_bytes):
     b = x.shape[0]
     y = torch.full((b, n), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
     st = g._lib.quant_gemv(fmt, w.data_ptr(), n, k, x.data_ptr(), k, y.data_ptr(), n, b,
                            ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
     assert st == 0, g._lib.ggq_status_string(st)
