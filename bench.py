@@ -7,16 +7,20 @@ with Q8_0 weights -- QKV 3072x2048, O 2048x2048, gate and up 6144x2048, down
 size is one grouped launch over the six matrices (README "Components": kernel
 fusion).  Weights and activations are seeded synthetic tensors with the model's
 shapes, resident in HBM before the timed region.  The weights are cycled over
-enough distinct device copies (>= 1 GiB) that no step finds them in the 256 MB
-last-level cache.  Steps are replayed from HIP graphs -- one graph runs a step
-on each weight copy in turn -- so the host's launch cost is not what is
-measured.
+enough distinct device copies (>= 1 GiB); step c runs its batch-1 launch on
+copy c and its batch-8 launch on copy c + copies/2, so no launch finds its
+weights in the 256 MB last-level cache.  Steps are replayed from HIP graphs --
+one graph runs a step on each weight copy in turn -- so the host's launch cost
+is not what is measured.
 
-Prints one JSON line: weight GB/s of the step (value), the dominant kernel's
-achieved bandwidth against the 8 TB/s HBM peak (roofline; per-launch HIP events on
-the launch stream), and the CPU oracle's rate on a bounded sample (cpu_baseline).
-Secondary figures (Q4_K GEMV, routed MoE, pp512 GEMM TFLOP/s) are reported under
-"secondary" unless --no-secondary is given.
+Prints one JSON line: weight GB/s of the step (value), the dominant launch's
+achieved bandwidth against the 8 TB/s HBM peak (roofline: HIP events on the
+launch stream around graph replays of that launch alone, back to back over the
+weight copies, so the time per launch includes the in-graph gaps between
+dependent kernels), and the CPU oracle on bounded samples of every
+configuration, 1 thread and all threads (cpu_baseline).  Secondary figures
+(the 1024x1024 and Q4_K GEMVs, routed MoE, pp512 GEMM TFLOP/s) are reported
+under "secondary" unless --no-secondary is given.
 """
 from __future__ import annotations
 
@@ -43,10 +47,11 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="weight copies to cycle (0 = auto, >= 1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-reps", type=int, default=5, help="timed oracle runs per sample (median)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device copy of known size (HBM counter calibration)")
-    p.add_argument("--only", choices=["q4k", "moe", "moe_prompt", "ffn", "gemm", "sweep", "hbm"],
+    p.add_argument("--only", choices=["small", "q4k", "moe", "moe_prompt", "ffn", "gemm", "sweep",
+                                      "hbm"],
                    default=None,
                    help="run one secondary workload only (for profiling)")
     return p.parse_args()
@@ -132,7 +137,10 @@ def main():
     weight_bytes_step = 2 * set_bytes
 
     def step_fn(c):
-        g1, g8 = groups[c]
+        # batch 8 on the copy half a cycle away: its weights were last read
+        # about copies/2 * 194 MB earlier, past the last-level cache
+        g1 = groups[c][0]
+        g8 = groups[(c + copies // 2) % copies][1]
         return lambda: (g1(), g8())
 
     # One graph runs a step on every weight copy in turn (`copies` steps per
@@ -163,7 +171,11 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = weight_bytes_step / (ms_step * 1e-3) / 1e9
 
-    # ---- per-launch HIP events on the launch stream (eager, same launches) ----
+    # ---- per-launch times: each launch kind alone, back to back over the
+    # weight copies in one graph, HIP events on the launch stream around the
+    # replays (the time per launch includes the in-graph gaps between its
+    # kernels and the next launch's) ----
+    del graphs
     agg = {}
     alg = {}
     for b_i, label in ((0, "gemv_q8_0_grouped_b1"), (1, "gemv_q8_0_grouped_b8")):
@@ -171,20 +183,12 @@ def main():
         alg[label] = grp0.weight_bytes + sum(
             xs[(name, grp0.batch)].numel() * 4 + ys[(name, grp0.batch)].numel() * 4
             for name, _, _ in shapes)
-    evs = []
-    for i in range(args.steps):
-        for b_i, label in ((0, "gemv_q8_0_grouped_b1"), (1, "gemv_q8_0_grouped_b8")):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            groups[i % copies][b_i]()
-            e1.record()
-            evs.append((label, e0, e1))
-    torch.cuda.synchronize()
-    for label, e0, e1 in evs:
-        t, c = agg.get(label, (0.0, 0))
-        agg[label] = (t + e0.elapsed_time(e1), c + 1)
-    dom = max(agg, key=lambda k: agg[k][0])
+        lgraph = capture(torch, [lambda: [groups[c][b_i]() for c in range(copies)]])
+        reps = max(2, args.steps // copies)
+        ms = replay_ms(torch, lgraph, reps, copies)
+        agg[label] = (ms * reps * copies, reps * copies)
+        del lgraph
+    dom = max(agg, key=lambda k: agg[k][0] / agg[k][1])
     dom_ms, dom_n = agg[dom]
     avg_ms = dom_ms / dom_n
     achieved = alg[dom] / (avg_ms * 1e-3) / 1e9
@@ -226,14 +230,17 @@ def main():
             "alg_bytes_per_launch": alg[dom],
             "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches": dom_n,
+            "timing": "HIP events around graph replays of this launch alone over the weight "
+                      "copies; includes in-graph launch gaps (kernel-only durations: rocprof "
+                      "summary under profiles/)",
         },
         "kernels": per_kernel,
     }
-    del graphs
     if not args.no_secondary:
         result["secondary"] = secondary(g, torch, synth)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(synth, shapes, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(synth, args.cpu_reps,
+                                              result.get("secondary"), value, alg, per_kernel)
     print(json.dumps(result), flush=True)
 
 
@@ -257,16 +264,21 @@ def calibrate_copy(torch):
     return {"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "reps": COPY_REPS}
 
 
+# The sources the layer-set launches are built from (their kernels, the shared
+# device helpers, the dispatch and its plans) and the build flags.
+LAYER_SET_SOURCES = ("api.hip", "gemv.hip", "gemv_core.h", "gemv_mfma.hip", "gemv_mfma_core.h",
+                     "ggq_device.h", "ggq_launch.h")
+
+
 def kernel_sources_digest():
-    """sha256 over the native sources and build flags; counter-derived traffic is reported only
-    while it matches the sources the counters were taken from."""
+    """sha256 over the layer-set launches' sources and build flags; counter-derived
+    traffic is reported only while it matches the sources the counters were taken from."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_gguf_q8_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in LAYER_SET_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     with open(os.path.join(ROOT, "quantized_gguf_q8_amd", "build.py"), "rb") as f:
         h.update(b"build.py\0" + f.read())   # compiler flags change the code too
     return h.hexdigest()
@@ -319,6 +331,33 @@ def secondary(g, torch, synth, only=None):
             "note": "torch device copy (read + write bytes) and torch.sum (read bytes), 1 GiB each",
         }
         del src, dst, acc
+    if only in (None, "small"):
+        # the 1024 x 1024 Q8_0 single-token product (batch 1 on the vector
+        # units; batch 8 through the single-launch matrix-core path); one
+        # call is one launch, replayed 16 to a graph over >= 1 GiB of copies
+        res = {}
+        n = k = 1024
+        w = synth.q8_0_matrix(n, k, seed=0, tensor_id=synth.tid(3, n, k))
+        copies = max(2, -(-ROTATE_BYTES // w.nbytes))
+        wd = torch.from_numpy(w).to(dev)
+        cps = [wd.clone() for _ in range(copies)]
+        for b in (1, 8):
+            x = torch.from_numpy(synth.normal_f32((b, k), 0, synth.tid(3, n, k) + b)).to(dev)
+            y = torch.empty((b, n), dtype=torch.float32, device=dev)
+            calls = [g.GemvGroup(g.Q8_0, [(c, n, k, x, y)], ws=None if b == 1 else "auto")
+                     for c in cps]
+            per = 16
+            fns = [(lambda j0: (lambda: [calls[(j0 + j) % copies]() for j in range(per)]))(j0)
+                   for j0 in range(0, copies, per)]
+            graphs = capture(torch, fns)
+            ms = replay_ms(torch, graphs, 2 * len(graphs), per)
+            gbs = w.nbytes / (ms * 1e-3) / 1e9
+            res[f"q8_0_{n}x{k}_b{b}"] = {"us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                        "alg_bytes": int(w.nbytes + 8 * b * k)}
+            del graphs, calls
+        del cps, wd
+        out["q8_0_gemv_small"] = res
     if only in (None, "q4k"):
         res = {}
         for name, n, k in synth.Q4K_FFN_PAIR:
@@ -517,32 +556,130 @@ def secondary(g, torch, synth, only=None):
     return out
 
 
-def cpu_baseline(synth, shapes, seconds):
-    """The oracle (fp64 C loops) on the same layer set, batch 1 then batch 8,
-    repeated until `seconds` have passed (at least one full pass)."""
+def _cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
+def _median_time(fn, reps):
+    fn()   # warm-up
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def cpu_baseline(synth, reps, secondary, value, alg, per_kernel):
+    """The oracle (plain C, fp64 accumulation) on bounded samples of every
+    configuration, with 1 thread and with all the threads the host gives one GPU
+    (rows or columns split across threads), median of `reps` runs after one
+    warm-up.  Rates use the same algorithmic units as the GPU figures (weight
+    bytes of the sample, or 2*M*N*K flop), so each row sits next to its GPU
+    number.  A reported baseline, not the target."""
+    import numpy as np
     import oracle
 
-    threads = oracle.default_threads()
-    host_w = [synth.q8_0_matrix(n, k, seed=0, tensor_id=synth.tid(1, n, k)) for _, n, k in shapes]
-    xs = {(name, b): synth.normal_f32((b, k), seed=0, tensor_id=synth.tid(1, n, k) + b)
-          for name, n, k in shapes for b in (1, 8)}
-    done_bytes = 0
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        for b in (1, 8):
-            for (name, n, k), w in zip(shapes, host_w):
-                oracle.gemv(synth.FMT_Q8_0, w, n, k, xs[(name, b)], threads=threads)
-                done_bytes += w.nbytes
-        passes += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the layer set at batch 1 and 8 "
-                      f"({done_bytes} weight bytes) in {el:.1f} s, fp64 oracle, "
-                      f"{threads} threads over row ranges"}
+    model, nproc = _cpu_info()
+    # the box's CPU share for one GPU is 16 threads, whatever nproc reports
+    full = max(1, min(nproc, 16))
+    rows = []
+    sec = secondary or {}
+
+    def add(config, unit, work, sample, fn_for, gpu=None):
+        r = {"config": config, "unit": unit, "sample": sample}
+        for th in (1, full):
+            t = _median_time(lambda: fn_for(th), reps)
+            r[f"threads_{th}"] = round(work / t / (1e9 if unit in ("GB/s", "GFLOP/s") else 1), 3)
+        r["gpu"] = gpu
+        rows.append(r)
+        return r
+
+    # the 1024 x 1024 Q8_0 GEMV: the whole matrix, batch 1
+    n = k = 1024
+    w = synth.q8_0_matrix(n, k, seed=0, tensor_id=synth.tid(3, n, k))
+    x = synth.normal_f32((1, k), 0, synth.tid(3, n, k) + 1)
+    add("q8_0_gemv_1024x1024_b1", "GB/s", w.nbytes, "whole matrix",
+        lambda th: oracle.gemv(synth.FMT_Q8_0, w, n, k, x, threads=th),
+        sec.get("q8_0_gemv_small", {}).get("q8_0_1024x1024_b1", {}).get("GB/s"))
+    # the layer set at batch 1 and 8: the first 1/8 of every matrix's rows
+    sets = []
+    for name, n, k in synth.DENSE_1B_LAYER_SET:
+        w = synth.q8_0_matrix(n, k, seed=0, tensor_id=synth.tid(1, n, k))
+        sets.append((name, n // 8, k, np.ascontiguousarray(w[: n // 8])))
+    wb = sum(ws.nbytes for _, _, _, ws in sets)
+    for b in (1, 8):
+        xs = {name: synth.normal_f32((b, k), seed=0, tensor_id=synth.tid(1, n * 8, k) + b)
+              for name, n, k, _ in sets}
+
+        def run(th, xs=xs):
+            for name, n, k, ws in sets:
+                oracle.gemv(synth.FMT_Q8_0, ws, n, k, xs[name], threads=th)
+        label = f"gemv_q8_0_grouped_b{b}"
+        gpu = per_kernel.get(label, {}).get("GB/s")
+        add(f"q8_0_layer_set_b{b}", "GB/s", wb, f"first 1/8 of each matrix's rows ({wb} B)",
+            run, gpu)
+    # the Q4_K pair at batch 1, 4, 16: the first 1/16 of the rows
+    for name, n, k in synth.Q4K_FFN_PAIR:
+        w = synth.q4_k_matrix(n, k, seed=0, tensor_id=synth.tid(2, n, k))
+        ns = n // 16
+        ws = np.ascontiguousarray(w[:ns])
+        for b in (1, 4, 16):
+            x = synth.normal_f32((b, k), 0, synth.tid(2, n, k) + 1)
+            add(f"q4k_gemv_{n}x{k}_b{b}", "GB/s", ws.nbytes, f"first {ns} of {n} rows",
+                lambda th, ws=ws, ns=ns, k=k, x=x: oracle.gemv(synth.FMT_Q4_K, ws, ns, k, x,
+                                                              threads=th),
+                sec.get("q4k_gemv", {}).get(f"{name}_{n}x{k}_b{b}", {}).get("GB/s"))
+    # the routed layer: 1 token (whole layer) and the first 4 of 16 tokens
+    e, h, f, top = synth.MOE_EXPERTS, synth.MOE_HIDDEN, synth.MOE_FFN, synth.MOE_TOP_K
+    for t, ts in ((1, 1), (16, 4)):
+        mo = synth.moe_layer(seed=0, n_tokens=t)
+        xs = mo["x"][:ts]
+        lg, _ = oracle.router_logits(mo["wr"], xs)
+        idx = oracle.topk(lg, top)
+        probs = oracle.route_probs(lg, idx)
+        per_expert = mo["wg"][0].nbytes + mo["wu"][0].nbytes + mo["wd"][0].nbytes
+        work = len(set(idx.ravel().tolist())) * per_expert + mo["wr"].nbytes
+
+        def run(th, mo=mo, xs=xs):
+            l2, _ = oracle.router_logits(mo["wr"], xs)
+            i2 = oracle.topk(l2, top)
+            oracle.moe(synth.FMT_Q4_K, mo["wg"], mo["wu"], mo["wd"], e, h, f, xs, i2,
+                       oracle.route_probs(l2, i2), threads=th)
+        add(f"moe_q4k_t{t}", "GB/s", work,
+            f"tokens 0..{ts - 1} of {t}: routing and expert layer, {work} weight bytes", run,
+            sec.get("moe_q4k", {}).get(f"t{t}", {}).get("GB/s"))
+    # the pp512 GEMMs: 16 output columns of all 512 rows
+    for name, fmt, n, k in synth.PP512_GEMMS:
+        tid = synth.tid(4, n, k)
+        w = synth.quant_matrix(fmt, n, k, seed=0, tensor_id=tid)
+        a = synth.normal_f32((synth.PP512_M, k), 0, tid + 1)
+        cols = list(range(16))
+        add(f"pp512_gemm_{name}", "GFLOP/s", 2.0 * synth.PP512_M * len(cols) * k,
+            f"{len(cols)} of {n} output columns, all {synth.PP512_M} rows",
+            lambda th, w=w, n=n, k=k, a=a, fmt=fmt: oracle.gemm_columns(fmt, w, n, k, a, cols,
+                                                                        threads=th),
+            (lambda r: None if r is None else round(r * 1e3, 1))(
+                sec.get("pp512_gemm", {}).get(name, {}).get("TFLOP/s")))
+    head = next(r for r in rows if r["config"] == "q8_0_layer_set_b1")
+    head8 = next(r for r in rows if r["config"] == "q8_0_layer_set_b8")
+    # the headline rate: the layer-set step (batch 1 then batch 8) with all threads
+    step = 2.0 / (1.0 / head[f"threads_{full}"] + 1.0 / head8[f"threads_{full}"])
+    return {"value": round(step, 3), "unit": "GB/s", "cores": full, "kind": "oracle",
+            "sample": "layer set, batch 1 then batch 8, first 1/8 of each matrix's rows; "
+                      f"median of {reps} runs after one warm-up, {full} threads",
+            "nproc": nproc, "cpu_model": model, "gpu_value": round(value, 2),
+            "configs": rows}
 
 
 if __name__ == "__main__":

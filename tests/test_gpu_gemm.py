@@ -3,7 +3,8 @@ within 8e-3 * sum|a w| of the fp64 oracle.
 
 phobos-bench pp<N> (README "Command-Line Tools") measures prompt batches; the
 full pp512 shapes are checked on sampled rows and columns the way the README's
-cluster_correctness example sample-checks a large product against the CPU.
+cluster_correctness example sample-checks a large product against the CPU, and
+on every output by a slow test.
 """
 import numpy as np
 import pytest
@@ -61,6 +62,23 @@ def test_gemm_pp512_sampled(g, name, fmt, n, k):
     cc, ss = oracle.gemm_columns(fmt, w, n, k, a, cols)
     worst = check_rel(c[:, cols], cc, ss, GEMM_TOL, f"{name} columns")
     say(f"  worst err / bound (columns) = {worst:.3g}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,fmt,n,k", synth.PP512_GEMMS)
+def test_gemm_pp512_every_output(g, name, fmt, n, k):
+    """Full-size pp512 products, every one of the 512 x N outputs against the
+    oracle (about 45 G multiply-adds in fp64 per product: ~10 s on 16 threads)."""
+    say(f"gemm pp512 every output {name}")
+    m = synth.PP512_M
+    tid = synth.tid(4, n, k)
+    w = synth.quant_matrix(fmt, n, k, seed=0, tensor_id=tid)
+    a = synth.normal_f32((m, k), seed=0, tensor_id=tid + 1)
+    c = host(g.quant_gemm(fmt, dev(w), n, k, dev(a)))
+    cr, s = oracle.gemm(fmt, w, n, k, a)
+    assert not np.isnan(cr).any()
+    worst = check_rel(c, cr, s, GEMM_TOL, f"{name} all outputs")
+    say(f"  worst err / bound = {worst:.3g}")
 
 
 @pytest.mark.parametrize("m", [17, 128, 2048])
