@@ -12,15 +12,17 @@
 //  1. each lane issues the loads of all of its wave's weight bytes (straight into
 //     registers, in the layout the MFMA B operand needs: lane (j, h) of a 16-row
 //     tile holds row j's bytes for k-octet h), then
-//  2. while they are in flight the workgroup splits its slice of the
-//     activations into exact fp16 (hi, lo) pairs in LDS: each batch row b is
-//     scaled by a power of two 2^S_b from the largest |x| of the slice (so the
-//     largest lands in [2^14, 2^15)), hi = fp16(x'), lo = fp16(x' - hi),
+//  2. while they are in flight each wave splits its unit's activations into
+//     exact fp16 (hi, lo) pairs in its own LDS region: each batch row b is
+//     scaled by a power of two 2^S_b from the largest |x| of the wave's 256
+//     columns (so the largest lands in [2^14, 2^15)), hi = fp16(x'),
+//     lo = fp16(x' - hi); no other wave reads them, so no barrier is needed,
 //  3. the products: v_mfma_f32_16x16x32_f16, A = activation pairs (rows 2b: hi,
 //     2b+1: lo), B = the decoded weights (Q8_0: q, scaled by d per 32-column
 //     block; Q4_K: sc*q <= 945, exact in fp16, scaled by d per super-block, the
 //     min term as one 16x16x16 MFMA of m_j against the sub-block sums of x),
-//  4. the four waves' partial sums are added in wave order and scaled by 2^-S_b.
+//  4. each wave scales its sums by 2^-S_b (exact) and the four waves' sums are
+//     added in wave order.
 // Rows too few to fill the chip are cut along K: the workgroups of a row tile
 // write their sums to the workspace (device-coherent stores), wait for them to
 // complete, count themselves on the tile's counter (one atomic add), and the
@@ -62,7 +64,7 @@ struct KsCfg {
     static constexpr int RED = T * MT * 64 * 8;                // one wave's (v0, v1) sums
     static_assert(RED <= UNIT, "a wave's sums fit its own fragment region");
     static constexpr int kLds = kKsWaves * UNIT;
-    static constexpr int PP = 4 * MT;                          // activation pieces per thread
+    static constexpr int PP = 4 * MT;                          // activation pieces per lane
 };
 
 // Raw weight bytes of one 16-row tile of a unit, per lane (j, h).
@@ -138,19 +140,6 @@ constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
 constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
 
-// Largest value over the wave (non-negative inputs), the same in every lane.
-__device__ __forceinline__ float wave_max_nonneg(float m) {
-    m = fmaxf(m, dpp_f<kDppXor1>(m));
-    m = fmaxf(m, dpp_f<kDppXor2>(m));
-    m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
-    m = fmaxf(m, dpp_f<kDppMirror>(m));
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
 __device__ __forceinline__ void scale_of(float m, float& sc, float& inv) {
     sc = 1.f;
     inv = 1.f;
@@ -162,18 +151,19 @@ __device__ __forceinline__ void scale_of(float m, float& sc, float& inv) {
     }
 }
 
-// The workgroup's activation slice: piece p = (batch row b, unit u, 8-column
-// group g) of thread tid is p = tid + 256 i.  These loads are issued before the
-// weight loads: the load counter drains in issue order, so the activation
-// split can then start while the weights are still in flight.
+// The wave's activation slice (its unit's 256 columns of every batch row):
+// piece q = (batch row b, 8-column group g) of lane l is q = l + 64 i, so each
+// load instruction reads two rows' 1 KiB runs.  These loads are issued before
+// the weight loads: the load counter drains in issue order, so the split can
+// start while the weights are still in flight.
 template <int MT>
-__device__ __forceinline__ void ks_load_x(const KsArgs& a, int kc0, int tid, uint4 (&xr)[4 * MT][2]) {
+__device__ __forceinline__ void ks_load_x(const KsArgs& a, int kc0, int lane, uint4 (&xr)[4 * MT][2]) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.batch * a.ldx * 4));
 #pragma unroll
     for (int i = 0; i < 4 * MT; ++i) {
-        const int p = tid + 256 * i;
-        const int b = p >> 7, u = (p >> 5) & 3, g = p & 31;
-        const int col = kc0 + kKsUnit * u + 8 * g;
+        const int q = lane + 64 * i;
+        const int b = q >> 5, g = q & 31;
+        const int col = kc0 + 8 * g;
         const bool ok = b < a.batch && col < a.k;
         const uint32_t off = (uint32_t)(b * a.ldx + col) * 4;
         xr[i][0] = buf_load16<false>(rx, ok ? off : kOob);
@@ -190,63 +180,65 @@ __device__ __forceinline__ int frag_slot(int i, int h, int s) {
     return ((i + 2 * s + (h & 1)) & 15) + 16 * h;
 }
 
-// Activation slice of this workgroup -> fp16 (hi, lo) A fragments in LDS, one
-// region per unit: [step][M tile][slot][8 halves] (slot = frag_slot), then
-// (Q4_K) the sub-block sums [M tile][lane][4 halves] for the 16x16x16 min
-// product.
+// The wave's activation slice -> fp16 (hi, lo) A fragments in the wave's LDS
+// region: [step][M tile][slot][8 halves] (slot = frag_slot), then (Q4_K) the
+// sub-block sums [M tile][lane][4 halves] for the 16x16x16 min product.
+// rmax[i][hf] returns the largest |x| of batch row 2i + hf (uniform).
 template <int FMT, int MT>
-__device__ __forceinline__ void ks_prep_x(const uint4 (&xr)[4 * MT][2], uint8_t* lds,
-                                          uint32_t* smax, int tid) {
+__device__ __forceinline__ void ks_prep_x(const uint4 (&xr)[4 * MT][2], uint8_t* ureg, int lane,
+                                          float (&rmax)[4 * MT][2]) {
     using C = KsCfg<FMT, MT, 1>;
-    float xv[C::PP][8];
+    const int g = lane & 31, hf = lane >> 5;
+    int s, h;
+    piece_slot<FMT>(g, s, h);
 #pragma unroll
     for (int i = 0; i < C::PP; ++i) {
+        // an empty statement that takes the piece and may touch memory: the
+        // weight loads before it stay before it, and the arithmetic on the piece
+        // cannot be hoisted above them
         const float4 f0 = __builtin_bit_cast(float4, xr[i][0]);
         const float4 f1 = __builtin_bit_cast(float4, xr[i][1]);
-        xv[i][0] = f0.x; xv[i][1] = f0.y; xv[i][2] = f0.z; xv[i][3] = f0.w;
-        xv[i][4] = f1.x; xv[i][5] = f1.y; xv[i][6] = f1.z; xv[i][7] = f1.w;
-    }
-    // largest |x| per batch row: the pieces of piece slot i in one wave share b
-#pragma unroll
-    for (int i = 0; i < C::PP; ++i) {
+        float xv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        asm volatile("" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]),
+                     "+v"(xv[5]), "+v"(xv[6]), "+v"(xv[7]) : : "memory");
+        // largest |x| of each of the two rows (lanes 0-31: row 2i, 32-63: 2i+1)
         float m = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(xv[i][c]));
-        m = wave_max_nonneg(m);
-        if ((tid & 63) == 0) atomicMax(&smax[(tid + 256 * i) >> 7], __float_as_uint(m));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::PP; ++i) {
-        const int p = tid + 256 * i;
-        const int b = p >> 7, u = (p >> 5) & 3, g = p & 31;
+        for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(xv[c]));
+        m = fmaxf(m, dpp_f<kDppXor1>(m));
+        m = fmaxf(m, dpp_f<kDppXor2>(m));
+        m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+        m = fmaxf(m, dpp_f<kDppMirror>(m));
+        const int mi = __builtin_bit_cast(int, m);
+        rmax[i][0] = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(mi, 0)),
+                           __builtin_bit_cast(float, __builtin_amdgcn_readlane(mi, 16)));
+        rmax[i][1] = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(mi, 32)),
+                           __builtin_bit_cast(float, __builtin_amdgcn_readlane(mi, 48)));
         float sc, inv;
-        scale_of(__uint_as_float(smax[b]), sc, inv);
-        int s, h;
-        piece_slot<FMT>(g, s, h);
+        scale_of(hf ? rmax[i][1] : rmax[i][0], sc, inv);
+        const int b = 2 * i + hf;
         const int t = b >> 3, ih = 2 * (b & 7);
         f16x8 hi, lo;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const float v = xv[i][c] * sc;
+            const float v = xv[c] * sc;
             const _Float16 vh = (_Float16)v;
             hi[c] = vh;
             lo[c] = (_Float16)(v - (float)vh);
         }
-        uint8_t* frag = lds + u * C::UNIT + (s * MT + t) * 1024;
+        uint8_t* frag = ureg + (s * MT + t) * 1024;
         *reinterpret_cast<f16x8*>(frag + frag_slot(ih, h, s) * 16) = hi;
         *reinterpret_cast<f16x8*>(frag + frag_slot(ih + 1, h, s) * 16) = lo;
         if constexpr (FMT == kQ4_K) {
             // sub-block jb = g / 4 is pieces 4jb .. 4jb+3: four consecutive lanes
-            float sblk = ((xv[i][0] + xv[i][1]) + (xv[i][2] + xv[i][3])) +
-                         ((xv[i][4] + xv[i][5]) + (xv[i][6] + xv[i][7]));
+            float sblk = ((xv[0] + xv[1]) + (xv[2] + xv[3])) + ((xv[4] + xv[5]) + (xv[6] + xv[7]));
             sblk += dpp_f<kDppXor1>(sblk);
             sblk += dpp_f<kDppXor2>(sblk);
             if ((g & 3) == 0) {
                 const int jb = g >> 2, hq = jb >> 2;
                 const float v = sblk * (sc * (1.f / 32.f));
                 const _Float16 vh = (_Float16)v;
-                _Float16* mb = reinterpret_cast<_Float16*>(lds + u * C::UNIT + C::FRAG + t * 512);
+                _Float16* mb = reinterpret_cast<_Float16*>(ureg + C::FRAG + t * 512);
                 mb[(ih + 16 * hq) * 4 + (jb & 3)] = vh;
                 mb[(ih + 1 + 16 * hq) * 4 + (jb & 3)] = (_Float16)(v - (float)vh);
             }
@@ -254,11 +246,16 @@ __device__ __forceinline__ void ks_prep_x(const uint4 (&xr)[4 * MT][2], uint8_t*
     }
     if constexpr (FMT == kQ4_K) {
         // k = 8..15 of the 16x16x16 min product (lane groups 2, 3) are zero
-        for (int q = tid; q < kKsWaves * MT * 32; q += 256) {
-            const int u = q / (MT * 32), t = (q / 32) % MT, ln = 32 + (q & 31);
-            *reinterpret_cast<uint2*>(lds + u * C::UNIT + C::FRAG + t * 512 + ln * 8) = make_uint2(0, 0);
-        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            if (lane < 32)
+                *reinterpret_cast<uint2*>(ureg + C::FRAG + t * 512 + (32 + lane) * 8) = make_uint2(0, 0);
     }
+    // the wave reads these fragments itself: LDS operations of one wave complete
+    // in issue order, so only the compiler must keep the reads after the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int FMT, int MT, int T>
@@ -356,7 +353,6 @@ template <int FMT, int MT, int T>
 __global__ __launch_bounds__(256) void gemv_ks_kernel(const KsArgs a) {
     using C = KsCfg<FMT, MT, T>;
     extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ uint32_t smax[16];
     __shared__ int s_last;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -367,34 +363,47 @@ __global__ __launch_bounds__(256) void gemv_ks_kernel(const KsArgs a) {
     const int64_t r0 = (int64_t)tile * C::ROWS;
     const int unit = part * kKsWaves + wave;
     const bool live = unit < a.nunit;
+    uint8_t* ureg = lds + wave * C::UNIT;
 
-    // 1. the workgroup's activation slice (cache-resident), then this wave's
-    //    weight bytes, all requested before any arithmetic
+    // 1. the wave's activation slice (cache-resident), then its weight bytes,
+    //    all requested before any arithmetic
     uint4 xr[4 * MT][2];
-    ks_load_x<MT>(a, part * kKsCols, tid, xr);
+    ks_load_x<MT>(a, unit * kKsUnit, lane, xr);
     KsRaw<FMT> raw[T];
     ks_load_w<FMT, T>(a, r0, unit, live, j, h, raw);
-    if (tid < 16) smax[tid] = 0u;
-    __syncthreads();
-    // 2. activation pairs of the workgroup's columns
-    ks_prep_x<FMT, MT>(xr, lds, smax, tid);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. activation pairs of the wave's unit
+    float rmax[4 * MT][2];
+    ks_prep_x<FMT, MT>(xr, ureg, lane, rmax);
     // 3. products of this wave's unit
     f32x4 acc[T][MT];
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint8_t* ureg = lds + wave * C::UNIT;
     if (live) ks_products<FMT, MT, T>(ureg, raw, lane, h, acc);
-    // 4. D rows 4h .. 4h+3 of lane (j, h) = (batch 8m + 2h: hi, lo), (batch 8m + 2h + 1: hi, lo)
+    // 4. D rows 4h .. 4h+3 of lane (j, h) = (batch 8m + 2h: hi, lo), (batch
+    //    8m + 2h + 1: hi, lo), i.e. rows 2i, 2i + 1 of piece index i = 4m + h;
+    //    each scaled back by the wave's own 2^-S_b
     float2* red = reinterpret_cast<float2*>(ureg);
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int m = 0; m < MT; ++m) {
+        float m0 = rmax[4 * m][0], m1 = rmax[4 * m][1];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            red[(t * MT + m) * 64 + lane] = make_float2(acc[t][m][0] + acc[t][m][1],
-                                                        acc[t][m][2] + acc[t][m][3]);
+        for (int q = 1; q < 4; ++q) {
+            if (h == q) {
+                m0 = rmax[4 * m + q][0];
+                m1 = rmax[4 * m + q][1];
+            }
+        }
+        float sc, inv0, inv1;
+        scale_of(m0, sc, inv0);
+        scale_of(m1, sc, inv1);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            red[(t * MT + m) * 64 + lane] = make_float2((acc[t][m][0] + acc[t][m][1]) * inv0,
+                                                        (acc[t][m][2] + acc[t][m][3]) * inv1);
+    }
     __syncthreads();
 
     constexpr int SLOTS = T * MT * 64;
@@ -411,13 +420,6 @@ __global__ __launch_bounds__(256) void gemv_ks_kernel(const KsArgs a) {
                 v0[i] += v.x;
                 v1[i] += v.y;
             }
-            const int ln = q & 63, m = (q >> 6) % MT;
-            const int b0 = 8 * m + 2 * (ln >> 4);
-            float sc, inv0, inv1;
-            scale_of(__uint_as_float(smax[b0]), sc, inv0);
-            scale_of(__uint_as_float(smax[b0 + 1]), sc, inv1);
-            v0[i] *= inv0;
-            v1[i] *= inv1;
         }
     }
     if (a.parts == 1) {
@@ -468,10 +470,24 @@ __global__ __launch_bounds__(256) void gemv_ks_kernel(const KsArgs a) {
             const int rr = 16 * t + (ln & 15);
             const int64_t row = r0 + rr;
             const int b0 = 8 * m + 2 * (ln >> 4);
+            // eight parts' loads in flight at a time (an index past the last
+            // part re-reads the last one and is not added), summed in part order
             float s0 = 0.f, s1 = 0.f;
-            for (int pp = 0; pp < a.parts; ++pp) {
-                s0 += __hip_atomic_load(tp + pp * PB + b0 * C::ROWS + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s1 += __hip_atomic_load(tp + pp * PB + (b0 + 1) * C::ROWS + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int p0 = 0; p0 < a.parts; p0 += 8) {
+                float v0p[8], v1p[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float* src = tp + min(p0 + u, a.parts - 1) * PB + b0 * C::ROWS + rr;
+                    v0p[u] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v1p[u] = __hip_atomic_load(src + C::ROWS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (p0 + u < a.parts) {
+                        s0 += v0p[u];
+                        s1 += v1p[u];
+                    }
+                }
             }
             if (row < a.n) {
                 if (b0 < a.batch) a.y[(int64_t)b0 * a.ldy + row] = s0;
