@@ -92,9 +92,9 @@ __device__ __forceinline__ void ks_load_w(const KsArgs& a, int64_t r0, int unit,
         const bool ok = live && row < a.n;
         if constexpr (FMT == kQ4_K) {
             const uint32_t o = (uint32_t)row * a.rb + (uint32_t)unit * kQ4Bytes;
-            raw[t].hd = buf_load16<true>(rw, ok ? o : kOob);
-            raw[t].q0 = buf_load16<true>(rw, ok ? o + 16 + 32 * h : kOob);
-            raw[t].q1 = buf_load16<true>(rw, ok ? o + 32 + 32 * h : kOob);
+            raw[t].hd = buf_load16<false>(rw, ok ? o : kOob);
+            raw[t].q0 = buf_load16<false>(rw, ok ? o + 16 + 32 * h : kOob);
+            raw[t].q1 = buf_load16<false>(rw, ok ? o + 32 + 32 * h : kOob);
         } else {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
