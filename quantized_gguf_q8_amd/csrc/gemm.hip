@@ -495,6 +495,8 @@ size_t gemm_workspace_bytes(int type, int64_t m, int64_t n, int64_t k) {
 
 hipError_t launch_gemm(int type, const uint8_t* w, int64_t n, int64_t k, const float* a,
                        int64_t lda, int64_t m, float* c, int64_t ldc, void* ws, hipStream_t s) {
+    if (gemm_mid_applies(type, m, n, k))   // its workspace (M*K bf16) fits in this one
+        return launch_gemm_mid(type, w, n, k, a, lda, m, c, ldc, ws, s);
     const int64_t kp = kpad(k);
     uint16_t* abf = static_cast<uint16_t*>(ws);
     const int64_t total = mpad(m) * (kp / 8);

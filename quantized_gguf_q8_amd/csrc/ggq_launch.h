@@ -68,6 +68,14 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
 hipError_t launch_combine(const float* dbuf, const int32_t* idx, const float* probs, int64_t e,
                           int64_t h, int64_t t, int top_k, float* y, hipStream_t s);
 
+// quant_gemm for 17..kGemmMidRows rows (moe_gemm.hip's grouped tile as a dense
+// product), where it covers the device; A goes to bf16 at the start of ws.
+constexpr int64_t kGemmMidRows = 128;
+bool gemm_mid_applies(int type, int64_t m, int64_t n, int64_t k);
+size_t gemm_mid_ws_bytes(int64_t m, int64_t k);
+hipError_t launch_gemm_mid(int type, const uint8_t* w, int64_t n, int64_t k, const float* a,
+                           int64_t lda, int64_t m, float* c, int64_t ldc, void* ws, hipStream_t s);
+
 // Routed expert feed-forward at prompt batch (grouped matrix-core GEMMs).
 int64_t moe_gemm_slot_bound(int64_t e, int64_t p);
 int64_t moe_gemm_tile_bound(int64_t e, int64_t p);

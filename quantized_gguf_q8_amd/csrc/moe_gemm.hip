@@ -209,6 +209,10 @@ struct MgArgs {
     uint16_t* hout;          // gate/up: bf16 h [slot][ldo]
     float* dout;             // down: fp32 [pair][ldo]
     int64_t ldo;
+    // > 0: a dense product of that many activation rows (one "expert", slot i =
+    // row i, tiles of 64 rows in blockIdx order); hdr, tiles and spair unused
+    int32_t dense_m;
+    int32_t ksplit;          // dense only: K halves (1 or 2); otherwise 1
 };
 
 // Raw bytes one lane loads per 256-column chunk of one 16-row column tile:
@@ -354,12 +358,14 @@ __device__ __forceinline__ bf16x8 mg_decode(const MgRaw<FMT>& r, const MgScale& 
     return __builtin_bit_cast(bf16x8, o);
 }
 
-// LDS byte offset of the activation piece (product s, group g, lane l): lane
-// indices are XOR-ed with s so that the eight pieces of one row written by
-// eight neighbouring threads fall on distinct banks; a fragment read (64 lanes,
-// one (s, g)) is still a permutation of one contiguous KiB.
+// LDS byte offset of the activation piece (product s, group g of the tile's G,
+// lane l): lane indices are XOR-ed with s so that the eight pieces of one row
+// written by eight neighbouring threads fall on distinct banks; a fragment
+// read (64 lanes, one (s, g)) is still a permutation of one contiguous KiB.
+// One chunk of a G-group tile takes 8 * G KiB.
+template <int G>
 __device__ __forceinline__ int mg_lds_off(int s, int g, int l) {
-    return ((s * 4 + g) * 64 + (l ^ s)) * 16;
+    return ((s * G + g) * 64 + (l ^ s)) * 16;
 }
 
 // One tile (G 16-row groups of slots, G fixed at compile time so that the
@@ -367,9 +373,15 @@ __device__ __forceinline__ int mg_lds_off(int s, int g, int l) {
 // NMAT = 2: gate and up (wave w holds rows 16*(w*TPW + j) .. of both
 // matrices); NMAT = 1: one matrix.  NW waves per workgroup (4 and 8 measured
 // the same; 4 is used).
-template <int FMT, int NMAT, int TPW, int NW, int G>
-__device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0, int ex, int nt) {
+// DENSE: a plain product (slot i = activation row i = output row i, chunk
+// buffers sized for this tile's groups, optionally one of two K halves added
+// onto a zeroed output); otherwise the grouped expert layout.
+template <int FMT, int NMAT, int TPW, int NW, int G, bool DENSE>
+__device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0, int ex, int nt,
+                                        int split) {
     constexpr int NT = NMAT * TPW;
+    constexpr int GL = DENSE ? G : 4;        // groups in the chunk buffer layout
+    constexpr int ABUF = 8 * GL * kAFrag;    // one chunk of activations
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4;
@@ -398,7 +410,9 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     for (int i = 0; i < PPT; ++i) {
         const int slot = row0 + (tid >> 5) + 2 * NW * i;
         int src = slot;
-        if (p.adiv > 0) {
+        if constexpr (DENSE) {
+            src = slot < p.dense_m ? slot : -1;
+        } else if (p.adiv > 0) {
             const int pr = p.spair[slot];
             src = pr >= 0 ? pr / p.adiv : -1;
         }
@@ -406,13 +420,19 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     }
     // LDS destination of piece i: row r = tid/32 + 2*NW*i lies in group r/16 at
     // row r%16, so the offsets differ from piece 0's by constants
-    const int adst0 = mg_lds_off(us, 0, (tid >> 5) + 16 * uq);
+    const int adst0 = mg_lds_off<GL>(us, 0, (tid >> 5) + 16 * uq);
     auto adst = [&](int i) {
         return NW == 8 ? adst0 + i * kAFrag : adst0 + (i >> 1) * kAFrag + (i & 1) * 128;
     };
     u32x4 av[PPT];
-    const int nc = p.k / kKC;
-    auto load_a = [&](int c) {
+    // chunks c0 .. c0 + nc - 1 of K (a dense product may split K in two)
+    const int nc_all = p.k / kKC;
+    const int per = DENSE ? (nc_all + p.ksplit - 1) / p.ksplit : nc_all;
+    const int c0 = DENSE ? split * per : 0;
+    const int nc = min(per, nc_all - c0);
+    if (nc <= 0) return;
+    auto load_a = [&](int cr) {
+        const int c = c0 + cr;
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const uint32_t off = asrc[i] == kOob ? kOob : asrc[i] + (uint32_t)c * (kKC * 2);
@@ -425,7 +445,8 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     };
 
     MgRaw<FMT> rw[2][NT];
-    auto load_w = [&](int c, MgRaw<FMT> (&dst)[NT]) {
+    auto load_w = [&](int cr, MgRaw<FMT> (&dst)[NT]) {
+        const int c = c0 + cr;
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -447,7 +468,7 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
             bf16x8 af[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                if (g < G) af[g] = *reinterpret_cast<const bf16x8*>(buf + mg_lds_off(S, g, lane));
+                if (g < G) af[g] = *reinterpret_cast<const bf16x8*>(buf + mg_lds_off<GL>(S, g, lane));
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const bf16x8 bw = mg_decode<FMT, S>(cw[j], sc[j]);
@@ -486,8 +507,8 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     auto step = [&](int c, const MgRaw<FMT> (&cur)[NT], MgRaw<FMT> (&nxt)[NT]) {
         load_a(c + 1);
         load_w(c + 1, nxt);
-        compute(lds + (c & 1) * kABuf, cur);
-        store_a(lds + ((c + 1) & 1) * kABuf);
+        compute(lds + (c & 1) * ABUF, cur);
+        store_a(lds + ((c + 1) & 1) * ABUF);
         __syncthreads();
     };
     int c = 0;
@@ -497,9 +518,9 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
     }
     if (c + 1 < nc) {
         step(c, rw[0], rw[1]);
-        compute(lds + ((c + 1) & 1) * kABuf, rw[1]);
+        compute(lds + ((c + 1) & 1) * ABUF, rw[1]);
     } else {
-        compute(lds + (c & 1) * kABuf, rw[0]);
+        compute(lds + (c & 1) * ABUF, rw[0]);
     }
 
     // D layout: lane holds rows 4*(lane/16) + r, column lane % 16 of each product
@@ -519,35 +540,53 @@ __device__ __forceinline__ void mg_tile(const MgArgs& p, uint8_t* lds, int row0,
                         (uint16_t)(cvt_bf16x2(hv, 0.f) & 0xFFFFu);
                 }
             } else {
-                const int pr = p.spair[slot];
+                const int pr = DENSE ? (slot < p.dense_m ? slot : -1) : p.spair[slot];
                 if (pr < 0) continue;
 #pragma unroll
-                for (int j = 0; j < TPW; ++j)
-                    if (col[j] < p.n) p.dout[(int64_t)pr * p.ldo + col[j]] = acc[g][j][r];
+                for (int j = 0; j < TPW; ++j) {
+                    if (col[j] >= p.n) continue;
+                    float* dst = p.dout + (int64_t)pr * p.ldo + col[j];
+                    // two K halves add onto a zeroed output: 0 + a + b is the
+                    // same in either order
+                    if (DENSE && p.ksplit > 1) unsafeAtomicAdd(dst, acc[g][j][r]);
+                    else *dst = acc[g][j][r];
+                }
             }
         }
     }
 }
 
-template <int FMT, int NMAT, int TPW, int NW>
+template <int FMT, int NMAT, int TPW, int NW, bool DENSE = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void mg_kernel(const MgArgs p) {
     extern __shared__ __align__(16) uint8_t lds[];
     // blocks go to the eight XCDs round robin: XCD x takes tiles x, x+8, ...,
     // each with all its column tiles in a row, so a tile's activations are
     // fetched into one L2 only
     const int b = blockIdx.x;
-    const int per = b >> 3;
-    const int mt = (per / p.ntn) * 8 + (b & 7);
-    const int nt = per % p.ntn;
-    if (mt >= p.hdr[0]) return;
-    const int row0 = p.tiles[2 * mt];
-    const int tinfo = p.tiles[2 * mt + 1];
+    int row0, tinfo, nt, split = 0;
+    if constexpr (DENSE) {
+        // dense: row tiles fastest, so each column tile's row tiles run side by
+        // side, then column tiles, then K halves
+        const int tiles = (p.dense_m + kBM - 1) / kBM;
+        const int mt = b % tiles;
+        nt = (b / tiles) % p.ntn;
+        split = b / tiles / p.ntn;
+        row0 = mt * kBM;
+        tinfo = min(4, (p.dense_m - row0 + kPad - 1) / kPad);
+    } else {
+        const int per = b >> 3;
+        const int mt = (per / p.ntn) * 8 + (b & 7);
+        nt = per % p.ntn;
+        if (mt >= p.hdr[0]) return;
+        row0 = p.tiles[2 * mt];
+        tinfo = p.tiles[2 * mt + 1];
+    }
     const int ex = tinfo >> 3;
     switch (tinfo & 7) {   // 16-row groups in this tile (1..4)
-        case 1: mg_tile<FMT, NMAT, TPW, NW, 1>(p, lds, row0, ex, nt); break;
-        case 2: mg_tile<FMT, NMAT, TPW, NW, 2>(p, lds, row0, ex, nt); break;
-        case 3: mg_tile<FMT, NMAT, TPW, NW, 3>(p, lds, row0, ex, nt); break;
-        default: mg_tile<FMT, NMAT, TPW, NW, 4>(p, lds, row0, ex, nt); break;
+        case 1: mg_tile<FMT, NMAT, TPW, NW, 1, DENSE>(p, lds, row0, ex, nt, split); break;
+        case 2: mg_tile<FMT, NMAT, TPW, NW, 2, DENSE>(p, lds, row0, ex, nt, split); break;
+        case 3: mg_tile<FMT, NMAT, TPW, NW, 3, DENSE>(p, lds, row0, ex, nt, split); break;
+        default: mg_tile<FMT, NMAT, TPW, NW, 4, DENSE>(p, lds, row0, ex, nt, split); break;
     }
 }
 
@@ -564,6 +603,60 @@ hipError_t launch_mg(MgArgs a, int64_t tile_bound, hipStream_t s) {
     const int64_t mt8 = (tile_bound + 7) / 8 * 8;
     hipLaunchKernelGGL((mg_kernel<FMT, NMAT, TPW, NW>), dim3((unsigned)(mt8 * a.ntn)), dim3(64 * NW),
                        2 * kABuf, s, a);
+    return hipGetLastError();
+}
+
+// A [M][K] fp32 (lda) -> bf16 [M][K], 8 values per thread; with `zero_n` > 0
+// also C [M][zero_n] (ldc) := 0 for the two K halves to add onto.
+__global__ __launch_bounds__(256) void mid_xbf_kernel(const float* __restrict__ a, int64_t lda,
+                                                      int64_t m, int64_t k,
+                                                      uint16_t* __restrict__ ab,
+                                                      float* __restrict__ c, int64_t ldc,
+                                                      int64_t zero_n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < m * zero_n) c[(i / zero_n) * ldc + i % zero_n] = 0.f;
+    const int64_t k8 = k / 8;
+    if (i >= m * k8) return;
+    const int64_t row = i / k8, c8 = i % k8;
+    const float4* src = reinterpret_cast<const float4*>(a + row * lda) + 2 * c8;
+    const float4 v0 = src[0], v1 = src[1];
+    uint4 o;
+    o.x = cvt_bf16x2(v0.x, v0.y);
+    o.y = cvt_bf16x2(v0.z, v0.w);
+    o.z = cvt_bf16x2(v1.x, v1.y);
+    o.w = cvt_bf16x2(v1.z, v1.w);
+    reinterpret_cast<uint4*>(ab + row * k)[c8] = o;
+}
+
+template <int FMT>
+hipError_t launch_mid_fmt(const uint8_t* w, int64_t n, int64_t k, const uint16_t* ab, int64_t m,
+                          float* c, int64_t ldc, int ksplit, hipStream_t s) {
+    MgArgs a{};
+    a.w[0] = w;
+    a.w[1] = w;
+    a.n = n;
+    a.rb = row_bytes_dev<FMT>(k);
+    a.k = (int32_t)k;
+    a.a = ab;
+    a.abytes = (uint32_t)(m * k * 2);
+    a.dout = c;
+    a.ldo = ldc;
+    a.dense_m = (int32_t)m;
+    a.ksplit = ksplit;
+    constexpr int NW = kMgWaves, TPW = 1;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(mg_kernel<FMT, 1, TPW, NW, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kABuf);
+        attr = true;
+    }
+    const int64_t ntn = (n + 16 * TPW * NW - 1) / (16 * TPW * NW);
+    const int64_t tiles = (m + kBM - 1) / kBM;
+    a.ntn = (int32_t)ntn;
+    // two chunk buffers of the largest tile (its groups of 16 rows)
+    const size_t lds = 2 * 8 * (size_t)std::min<int64_t>(4, (m + kPad - 1) / kPad) * kAFrag;
+    hipLaunchKernelGGL((mg_kernel<FMT, 1, TPW, NW, true>), dim3((unsigned)(tiles * ntn * ksplit)),
+                       dim3(64 * NW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -586,6 +679,7 @@ hipError_t launch_fmt(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, i
     a.spair = m.spair;
     a.hout = m.hb;
     a.ldo = f;
+    a.ksplit = 1;
     hipError_t err = launch_mg<FMT, 2, 1, kMgWaves>(a, tb, s);
     if (err != hipSuccess) return err;
     MgArgs d{};
@@ -602,6 +696,7 @@ hipError_t launch_fmt(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, i
     d.spair = m.spair;
     d.dout = m.dbuf;
     d.ldo = h;
+    d.ksplit = 1;
     return launch_mg<FMT, 1, 2, kMgWaves>(d, tb, s);
 }
 
@@ -625,6 +720,40 @@ hipError_t launch_moe_gemm(int type, const uint8_t* wg, const uint8_t* wu, const
                         : launch_fmt<kQ8_0>(wg, wu, wd, e, h, f, t, top_k, m, s);
     if (err != hipSuccess) return err;
     return launch_combine(m.dbuf, idx, probs, e, h, t, top_k, y, s);
+}
+
+constexpr int64_t kMidCUs = 256;
+
+// Products of a few tens of rows: the grouped kernel's tile (up to 64 rows of A
+// in LDS, the weights decoded straight into matrix-core operands) over column
+// tiles of 64 weight rows, A rounded to bf16 once.
+bool gemm_mid_applies(int type, int64_t m, int64_t n, int64_t k) {
+    if (type != kQ4_K && type != kQ8_0) return false;
+    if (m <= 16 || m > kGemmMidRows || k % kKC != 0 || k > INT32_MAX) return false;
+    if (m * k * 2 >= ((int64_t)1 << 31) || n * row_bytes(type, k) >= ((int64_t)1 << 32)) return false;
+    // enough column tiles to cover the compute units
+    const int64_t tiles = (m + kBM - 1) / kBM;
+    return (n + 63) / 64 * tiles >= 192;
+}
+
+size_t gemm_mid_ws_bytes(int64_t m, int64_t k) { return al256((size_t)m * k * 2); }
+
+hipError_t launch_gemm_mid(int type, const uint8_t* w, int64_t n, int64_t k, const float* a,
+                           int64_t lda, int64_t m, float* c, int64_t ldc, void* ws, hipStream_t s) {
+    uint16_t* ab = static_cast<uint16_t*>(ws);
+    // K in two halves (added onto a zeroed C) while the workgroups of both
+    // still fit the device at once: twice the loads in flight
+    const int64_t wgs = (m + kBM - 1) / kBM * ((n + 63) / 64);
+    const int64_t groups = std::min<int64_t>(4, (m + kPad - 1) / kPad);
+    const int64_t per_cu = std::min<int64_t>(3, (160 * 1024) / (2 * 8 * groups * kAFrag));
+    const int ksplit = (k / kKC >= 8 && 2 * wgs <= per_cu * kMidCUs) ? 2 : 1;
+    const int64_t cnt = std::max(m * (k / 8), ksplit > 1 ? m * n : (int64_t)0);
+    hipLaunchKernelGGL(mid_xbf_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s, a, lda,
+                       m, k, ab, c, ldc, ksplit > 1 ? n : (int64_t)0);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return type == kQ4_K ? launch_mid_fmt<kQ4_K>(w, n, k, ab, m, c, ldc, ksplit, s)
+                         : launch_mid_fmt<kQ8_0>(w, n, k, ab, m, c, ldc, ksplit, s);
 }
 
 }  // namespace ggq

@@ -81,6 +81,23 @@ def test_gemm_pp512_every_output(g, name, fmt, n, k):
     say(f"  worst err / bound = {worst:.3g}")
 
 
+# 17..128 rows run as the grouped-expert tile over 64-row column tiles (when
+# those cover the device): one and two row tiles, ragged last row group and
+# ragged last column tile, both formats.
+@pytest.mark.parametrize("fmt,m,n,k", [
+    (Q4, 17, 12304, 512), (Q8, 64, 12300, 256), (Q4, 65, 6200, 1024), (Q8, 128, 6144, 768),
+    (Q4, 100, 6150, 256), (Q8, 33, 12290, 512),
+])
+def test_gemm_mid_rows_full_check(g, fmt, m, n, k):
+    say(f"gemm mid rows fmt={fmt} m={m} n={n} k={k}")
+    w = synth.quant_matrix(fmt, n, k, seed=2, tensor_id=m + n)
+    a = synth.normal_f32((m, k), seed=2, tensor_id=m + n + 1)
+    c = host(g.quant_gemm(fmt, dev(w), n, k, dev(a)))
+    cr, s = oracle.gemm(fmt, w, n, k, a)
+    worst = check_rel(c, cr, s, GEMM_TOL, "gemm mid rows")
+    say(f"  worst err / bound = {worst:.3g}")
+
+
 @pytest.mark.parametrize("m", [17, 128, 2048])
 def test_gemm_prompt_sweep_sampled(g, m):
     """Prompt lengths around pp512 (the GEMV / GEMM crossover just past the
