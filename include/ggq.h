@@ -31,13 +31,14 @@
  *  - Arguments are validated on the host before any HIP call; an invalid call
  *    returns a negative ggq_status and enqueues nothing.  A launch failure returns
  *    GGQ_ERR_LAUNCH.  Device faults surface at the caller's next synchronisation.
- *  - Results are deterministic: the same inputs give the same bits.  The one
- *    use of floating-point atomics is in the matrix-core decode GEMV (quant_gemv
- *    and friends with a workspace, batch >= 2): a row tile whose K range is cut
- *    in two adds both halves with atomic adds onto an output that an earlier
- *    kernel of the same call zeroed.  0 + a + b gives the same bits in either
- *    order, so the result does not depend on which half lands first; deeper K
- *    cuts keep per-part sums in the workspace and add them in part order.
+ *  - Results are deterministic: the same inputs give the same bits.  Floating-
+ *    point atomics appear in two places, both as two adds onto an output that
+ *    an earlier kernel of the same call zeroed: the matrix-core decode GEMV
+ *    (quant_gemv and friends with a workspace, batch >= 2) when a row tile's K
+ *    range is cut in two, and quant_gemm at 17..128 rows when K is cut in two.
+ *    0 + a + b gives the same bits in either order, so the result does not
+ *    depend on which half lands first; deeper K cuts keep per-part sums in the
+ *    workspace and add them in part order.
  *  - Outputs never alias inputs or the workspace: y (or c, h) must not overlap
  *    w, x (or a) or ws.
  *  - Workspaces of quant_gemv, quant_gemv_grouped, quant_gemv_swiglu and
@@ -236,6 +237,10 @@ size_t quant_gemm_workspace_size(int type, int64_t m, int64_t n, int64_t k, int 
  * products accumulate in fp32 on the matrix cores.  Result within
  * 8e-3 * sum_c |a w| of the exact value.  Up to 16 rows (M <= 16) the product
  * runs as quant_gemv instead (one read of W; within its tighter 1e-5 bound).
+ * From 17 to 128 rows, when K is a multiple of 256 and the 64-row column tiles
+ * cover the device, all rows of a 64-row block share each weight read (A in
+ * bf16 staged through LDS, weights decoded straight into matrix-core operands;
+ * c is first zeroed when K is cut in two).
  *   a     device fp32 [M][lda], lda >= K, lda % 4 == 0, 16-byte aligned
  *   c     device fp32 [M][ldc], ldc >= N
  *   mode  GGQ_GEMM_BF16
