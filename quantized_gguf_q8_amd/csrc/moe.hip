@@ -44,11 +44,11 @@ constexpr int kMaxTopK = 32;
 // tokens (token groups spread over the grid's second dimension); per token a
 // lane keeps four component sums, combined pairwise, and the wave's lanes are
 // summed by a fixed butterfly.
+template <int kTok>
 __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restrict__ wr,
                                                             int64_t e, int64_t h,
                                                             const float* __restrict__ x,
                                                             int64_t t, float* __restrict__ logits) {
-    constexpr int kTok = 4;
     const int lane = threadIdx.x & 63;
     const int64_t ei = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (ei >= e) return;
@@ -56,20 +56,35 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
     const int64_t h4 = h / 4;
     // token groups of kTok are spread over blockIdx.y (and looped beyond that)
     for (int64_t t0 = (int64_t)blockIdx.y * kTok; t0 < t; t0 += (int64_t)gridDim.y * kTok) {
-        const int nt = (int)(t - t0 < kTok ? t - t0 : kTok);
+        const int nt = kTok == 1 ? 1 : (int)(t - t0 < kTok ? t - t0 : kTok);
         float p[kTok][4];
 #pragma unroll
         for (int j = 0; j < kTok; ++j) p[j][0] = p[j][1] = p[j][2] = p[j][3] = 0.f;
-        for (int64_t i = lane; i < h4; i += 64) {
-            const float4 a = w4[i];
+        // pieces lane, lane + 64, ... in order; kU of them requested at a time
+        // (a piece index past the row re-reads the last piece and is not added)
+        constexpr int kU = kTok == 1 ? 8 : 4;
+        for (int64_t i0 = lane; i0 < h4; i0 += 64 * kU) {
+            float4 a[kU], b[kU][kTok];
 #pragma unroll
-            for (int j = 0; j < kTok; ++j) {
-                if (j < nt) {
-                    const float4 b = reinterpret_cast<const float4*>(x + (t0 + j) * h)[i];
-                    p[j][0] += a.x * b.x;
-                    p[j][1] += a.y * b.y;
-                    p[j][2] += a.z * b.z;
-                    p[j][3] += a.w * b.w;
+            for (int u = 0; u < kU; ++u) {
+                const int64_t i = min(i0 + 64 * u, h4 - 1);
+                a[u] = w4[i];
+#pragma unroll
+                for (int j = 0; j < kTok; ++j)
+                    if (j < nt) b[u][j] = reinterpret_cast<const float4*>(x + (t0 + j) * h)[i];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (i0 + 64 * u < h4) {
+#pragma unroll
+                    for (int j = 0; j < kTok; ++j) {
+                        if (j < nt) {
+                            p[j][0] += a[u].x * b[u][j].x;
+                            p[j][1] += a[u].y * b[u][j].y;
+                            p[j][2] += a[u].z * b[u][j].z;
+                            p[j][3] += a[u].w * b[u][j].w;
+                        }
+                    }
                 }
             }
         }
@@ -1055,6 +1070,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // row's owner adds them up in (slot, piece) order.  Slots whose expert index
 // lies outside [0, E) contribute nothing and their weights are not read.
 constexpr int kD1Units = 4;
+// h of a slot is kept in LDS as 64-float pieces kD1Stride floats apart, so the
+// pieces that the lanes of a wave read at once start on different banks
+constexpr int kD1Stride = 68;
 
 struct Down1Args {
     const uint8_t* wd;     // [E][H][rb]
@@ -1080,8 +1098,8 @@ struct D1Raw<kQ8_0> {
 template <int FMT>
 __global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
     extern __shared__ __align__(16) uint8_t lds[];
-    float* lh = reinterpret_cast<float*>(lds);   // [top_k][F]
-    float* lpart = lh + a.top_k * a.f;          // one partial sum per unit
+    float* lh = reinterpret_cast<float*>(lds);   // [top_k][F / 64][kD1Stride]
+    float* lpart = lh + a.top_k * a.upr * kD1Stride;   // one partial sum per unit
     __shared__ int s_ex[kMaxTopK];
     __shared__ float s_p[kMaxTopK];
     const int tid = threadIdx.x;
@@ -1116,8 +1134,11 @@ __global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
     // h of every slot (rows of slots without an expert are copied too and never
     // used), the slots' experts and weights for the final sums
     const int hq = a.top_k * a.f / 4;
-    for (int i = tid; i < hq; i += 256)
-        reinterpret_cast<float4*>(lh)[i] = reinterpret_cast<const float4*>(a.h)[i];
+    for (int i = tid; i < hq; i += 256) {
+        const int c = 4 * i, slot = c / a.f, col = c % a.f;
+        *reinterpret_cast<float4*>(lh + (slot * a.upr + col / 64) * kD1Stride + col % 64) =
+            reinterpret_cast<const float4*>(a.h)[i];
+    }
     if (tid < a.top_k) {
         s_ex[tid] = a.idx[tid];
         s_p[tid] = a.probs[tid];
@@ -1132,7 +1153,7 @@ __global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
         if (live[j]) {
             const int slot = u / per_slot;
             const int piece = (u % per_slot) % a.upr;
-            const float* hv = lh + slot * a.f + 64 * piece;
+            const float* hv = lh + (slot * a.upr + piece) * kD1Stride;
             if constexpr (FMT == kQ4_K) {
                 // low nibbles: sub-block 2c, weights 64c + l; high: 2c + 1, 64c + 32 + l
                 const int c = piece % 4;
@@ -1450,9 +1471,13 @@ hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, i
                            dim3(128), 0, s, wr, e, h, x, t, logits);
     } else {
         const int64_t groups = (t + 3) / 4;
-        hipLaunchKernelGGL(router_logits_kernel,
-                           dim3((unsigned)((e + 3) / 4), (unsigned)(groups < 64 ? groups : 64)),
-                           dim3(256), 0, s, wr, e, h, x, t, logits);
+        if (t == 1)
+            hipLaunchKernelGGL((router_logits_kernel<1>), dim3((unsigned)((e + 3) / 4), 1), dim3(256), 0,
+                               s, wr, e, h, x, t, logits);
+        else
+            hipLaunchKernelGGL((router_logits_kernel<4>),
+                               dim3((unsigned)((e + 3) / 4), (unsigned)(groups < 64 ? groups : 64)),
+                               dim3(256), 0, s, wr, e, h, x, t, logits);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1522,7 +1547,7 @@ hipError_t launch_swiglu(int type, const uint8_t* wg, const uint8_t* wu, int64_t
 static bool down1_fits(int64_t f, int top_k) {
     // dynamic LDS (h of every slot, one partial per unit) plus the kernel's
     // static slot arrays within the default 64 KiB
-    return ((int64_t)top_k * f + (int64_t)kD1Units * 256 + 2 * kMaxTopK) * 4 <= 65536 &&
+    return ((int64_t)top_k * (f / 64) * kD1Stride + (int64_t)kD1Units * 256 + 2 * kMaxTopK) * 4 <= 65536 &&
            (int64_t)top_k * (f / 64) <= (int64_t)kD1Units * 256;
 }
 
@@ -1547,7 +1572,7 @@ static hipError_t launch_down1(int type, const uint8_t* wd, int64_t e, int64_t h
     const int64_t wgs = 2 * (int64_t)moe_device_cus();
     const int64_t spread = (hdim + wgs - 1) / wgs;
     a.rows = (int32_t)std::max<int64_t>(1, std::min<int64_t>({cap, spread, 256}));
-    const size_t lds = ((size_t)top_k * f + (size_t)top_k * a.rows * a.upr) * 4;
+    const size_t lds = ((size_t)top_k * a.upr * kD1Stride + (size_t)top_k * a.rows * a.upr) * 4;
     const unsigned grid = (unsigned)((hdim + a.rows - 1) / a.rows);
     if (type == kQ4_K)
         hipLaunchKernelGGL(moe_down1_kernel<kQ4_K>, dim3(grid), dim3(256), lds, s, a);
