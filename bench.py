@@ -399,7 +399,21 @@ def secondary(g, torch, synth, only=None):
             per_expert = mo["wg"][0].nbytes + mo["wu"][0].nbytes + mo["wd"][0].nbytes
             alg = distinct * per_expert + mo["wr"].nbytes
 
+            # the layer as one call (moe_layer_gemv: for one token the router and
+            # the selection are one launch), and as moe_route then moe_expert_gemv
+            lws = torch.zeros(g.moe_layer_workspace_size(e, t, k, h, f), dtype=torch.uint8,
+                              device=dev)
+            outs = (y, torch.empty((t, k), dtype=torch.int32, device=dev),
+                    torch.empty((t, k), dtype=torch.float32, device=dev),
+                    torch.empty((t, e), dtype=torch.float32, device=dev))
+
             def layer(c):
+                def run():
+                    wg_, wu_, wd_ = sets[c]
+                    g.moe_layer_gemv(g.Q4_K, wr, wg_, wu_, wd_, e, h, f, x, k, out=outs, ws=lws)
+                return run
+
+            def two_calls(c):
                 def run():
                     wg_, wu_, wd_ = sets[c]
                     ii, pp, _ = g.moe_route(wr, x, k)
@@ -409,10 +423,14 @@ def secondary(g, torch, synth, only=None):
             # one graph runs the layer once on every weight copy
             graphs = capture(torch, [lambda: [layer(c)() for c in range(copies)]])
             ms = replay_ms(torch, graphs, 50, copies)
+            del graphs
+            graphs = capture(torch, [lambda: [two_calls(c)() for c in range(copies)]])
+            ms2 = replay_ms(torch, graphs, 50, copies)
             gbs = alg / (ms * 1e-3) / 1e9
             res[f"t{t}"] = {"us": round(ms * 1e3, 3), "distinct_experts": distinct,
                             "alg_bytes": alg, "GB/s": round(gbs, 1),
-                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "route_then_experts_us": round(ms2 * 1e3, 3)}
             del graphs, sets
         out["moe_q4k"] = res
     if only in (None, "moe_prompt"):

@@ -41,10 +41,11 @@
  *    workspace and add them in part order.
  *  - Outputs never alias inputs or the workspace: y (or c, h) must not overlap
  *    w, x (or a) or ws.
- *  - Workspaces of quant_gemv, quant_gemv_grouped, quant_gemv_swiglu and
- *    quant_gemm begin with a control block of GGQ_CTRL_BYTES: per-row-tile
- *    counters through which the workgroups of a single-launch GEMV learn which
- *    of them adds up a tile's K parts.  It must be zero before a workspace is
+ *  - Workspaces of quant_gemv, quant_gemv_grouped, quant_gemv_swiglu,
+ *    quant_gemm and moe_layer_gemv begin with a control block of
+ *    GGQ_CTRL_BYTES: counters through which the workgroups of one launch learn
+ *    which of them finishes last (the one that adds up a tile's K parts, or
+ *    makes the expert selection).  It must be zero before a workspace is
  *    first used (allocate it zeroed, or clear those bytes once); every call
  *    leaves it zero, and the rest of the workspace may hold anything.  These
  *    calls can therefore share one workspace; a workspace that served other
@@ -310,6 +311,36 @@ int moe_expert_gemv(int type, const void *wg, const void *wu, const void *wd, in
 
 /* Byte offset of the hidden-state array h inside the moe_expert_gemv workspace. */
 size_t moe_workspace_h_offset(int64_t e, int64_t t, int top_k);
+
+/*
+ * moe_layer_workspace_size -- device workspace bytes moe_layer_gemv needs: the
+ * GGQ_CTRL_BYTES control block, then a moe_expert_gemv workspace.  0 on bad
+ * arguments.
+ */
+size_t moe_layer_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f);
+
+/*
+ * moe_layer_gemv -- moe_route followed by moe_expert_gemv on the same
+ * arguments (README opening paragraph: the router picks a few experts per
+ * token and only they take part), with identical results bit for bit: logits,
+ * idx, probs and y are what the two calls would write.  For one token the
+ * router and the selection are one launch (the last router workgroup to
+ * finish, counted in the control block, makes the selection), so the layer is
+ * three launches: routing, gate/up, down and combine.
+ *   type, e, h, f, x, t, top_k, y, wg, wu, wd   as for moe_expert_gemv
+ *   wr, logits, idx, probs                       as for moe_route (written)
+ *   ws     device workspace >= moe_layer_workspace_size(E, T, top_k, H, F)
+ *          bytes, 256-byte aligned, control block zero before the first call
+ *          (every call leaves it zero; the rest may hold anything); h is at
+ *          byte offset GGQ_CTRL_BYTES + moe_workspace_h_offset(E, T, top_k) on
+ *          return
+ * Calls that share a workspace must not overlap.  T == 0 is a no-op.
+ * Errors: GGQ_ERR_ARG, GGQ_ERR_ALIGN, GGQ_ERR_WORKSPACE, GGQ_ERR_UNSUPPORTED.
+ */
+int moe_layer_gemv(int type, const float *wr, const void *wg, const void *wu, const void *wd,
+                   int64_t e, int64_t h, int64_t f, const float *x, int64_t t, int top_k,
+                   float *logits, int32_t *idx, float *probs, float *y, void *ws,
+                   size_t ws_bytes, void *stream);
 
 /*
  * moe_gemm_workspace_size -- device workspace bytes moe_expert_gemm needs:

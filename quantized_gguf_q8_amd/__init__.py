@@ -59,6 +59,9 @@ _SIGS = {
     "moe_workspace_h_offset": (_SZ, [_I64, _I64, _I]),
     "moe_expert_gemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _P, _P,
                              _SZ, _P]),
+    "moe_layer_workspace_size": (_SZ, [_I64, _I64, _I, _I64, _I64]),
+    "moe_layer_gemv": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _I, _P, _P, _P, _P,
+                            _P, _SZ, _P]),
     "moe_gemm_workspace_size": (_SZ, [_I64, _I64, _I, _I64, _I64]),
     "moe_expert_gemm": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _P, _P,
                              _SZ, _P]),
@@ -349,6 +352,46 @@ def moe_expert_gemv(fmt: int, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tens
                                                 _ptr(x), t, _ptr(idx), _ptr(probs), top_k,
                                                 _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+def moe_layer_workspace_size(e: int, t: int, top_k: int, h: int, f: int) -> int:
+    return _lib.moe_layer_workspace_size(e, t, top_k, h, f)
+
+
+def moe_layer_gemv(fmt: int, wr: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor,
+                   wd: torch.Tensor, e: int, h: int, f: int, x: torch.Tensor, top_k: int,
+                   out: tuple | None = None, ws: torch.Tensor | None = None):
+    """moe_route then moe_expert_gemv (one token: routing in one launch).
+    Returns (y [T, H], idx int32 [T, k], probs [T, k], logits [T, E]); `out` may
+    give those four tensors to write.  A given `ws` must start with a zero
+    control block (torch.zeros); every call leaves it zero."""
+    _dev(wr, "wr", torch.float32)
+    _wbytes(wg, fmt, e * f, h, "wg")
+    _wbytes(wu, fmt, e * f, h, "wu")
+    _wbytes(wd, fmt, e * h, f, "wd")
+    _dev(x, "x", torch.float32)
+    t = x.shape[0]
+    if tuple(wr.shape) != (e, h) or x.shape[1] != h:
+        raise ValueError("wr, x disagree on E / H")
+    if out is None:
+        out = (torch.empty((t, h), dtype=torch.float32, device=x.device),
+               torch.empty((t, top_k), dtype=torch.int32, device=x.device),
+               torch.empty((t, top_k), dtype=torch.float32, device=x.device),
+               torch.empty((t, e), dtype=torch.float32, device=x.device))
+    y, idx, probs, logits = out
+    _dev(y, "y", torch.float32)
+    _dev(idx, "idx", torch.int32)
+    _dev(probs, "probs", torch.float32)
+    _dev(logits, "logits", torch.float32)
+    need = moe_layer_workspace_size(e, t, top_k, h, f)
+    if ws is None:
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(ws, "ws", torch.uint8)
+    _ck("moe_layer_gemv", _lib.moe_layer_gemv(fmt, _ptr(wr), _ptr(wg), _ptr(wu), _ptr(wd), e, h,
+                                              f, _ptr(x), t, top_k, _ptr(logits), _ptr(idx),
+                                              _ptr(probs), _ptr(y), _ptr(ws), ws.numel(),
+                                              _stream()))
+    return y, idx, probs, logits
 
 
 def moe_gemm_workspace_size(e: int, t: int, top_k: int, h: int, f: int) -> int:

@@ -345,6 +345,33 @@ int moe_expert_gemv(int type, const void* wg, const void* wu, const void* wd, in
                                     top_k, y, ws, as_stream(stream)));
 }
 
+size_t moe_layer_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
+    if (e < 1 || e > kMaxExperts || t < 1 || top_k < 1 || top_k > kMaxTopK || h < 1 || f < 1)
+        return 0;
+    return ggq::moe_layer_ws_bytes(e, t, top_k, h, f);
+}
+
+int moe_layer_gemv(int type, const float* wr, const void* wg, const void* wu, const void* wd,
+                   int64_t e, int64_t h, int64_t f, const float* x, int64_t t, int top_k,
+                   float* logits, int32_t* idx, float* probs, float* y, void* ws, size_t ws_bytes,
+                   void* stream) {
+    // the arguments of moe_route and of moe_expert_gemv
+    if (h > (1 << 24) || t > INT_MAX) return GGQ_ERR_ARG;
+    const int rc = check_moe(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y);
+    if (rc != GGQ_OK || t == 0) return rc;
+    if (!wr || !logits) return GGQ_ERR_ARG;
+    if (!aligned(wr, 16) || !aligned(logits, 4)) return GGQ_ERR_ALIGN;
+    const int64_t lim = (int64_t)1 << 32;
+    if (t * h * 4 >= lim || t * top_k * f * 4 >= lim || t * top_k * h * 4 >= lim)
+        return GGQ_ERR_ARG;
+    if (!ws || ws_bytes < ggq::moe_layer_ws_bytes(e, t, top_k, h, f)) return GGQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
+    return launched(ggq::launch_moe_layer(type, wr, static_cast<const uint8_t*>(wg),
+                                          static_cast<const uint8_t*>(wu),
+                                          static_cast<const uint8_t*>(wd), e, h, f, x, t, top_k,
+                                          logits, idx, probs, y, ws, as_stream(stream)));
+}
+
 size_t moe_gemm_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
     if (e < 1 || e > kMaxExperts || t < 1 || top_k < 1 || top_k > kMaxTopK || h < 1 || f < 1)
         return 0;

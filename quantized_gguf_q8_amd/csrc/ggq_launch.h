@@ -64,6 +64,14 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
                       const int32_t* idx, const float* probs, int top_k, float* y, void* ws,
                       hipStream_t s);
 
+// moe_route then moe_expert_gemv; one token: the router and the selection in
+// one launch.  Workspace: the control block, then the moe_expert_gemv workspace.
+size_t moe_layer_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f);
+hipError_t launch_moe_layer(int type, const float* wr, const uint8_t* wg, const uint8_t* wu,
+                            const uint8_t* wd, int64_t e, int64_t h, int64_t f, const float* x,
+                            int64_t t, int top_k, float* logits, int32_t* idx, float* probs,
+                            float* y, void* ws, hipStream_t s);
+
 // y[t] = sum_s probs[t][s] * dbuf[t*top_k + s] (slot order; out-of-range experts count 0).
 hipError_t launch_combine(const float* dbuf, const int32_t* idx, const float* probs, int64_t e,
                           int64_t h, int64_t t, int top_k, float* y, hipStream_t s);

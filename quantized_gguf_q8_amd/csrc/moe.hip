@@ -44,6 +44,37 @@ constexpr int kMaxTopK = 32;
 // tokens (token groups spread over the grid's second dimension); per token a
 // lane keeps four component sums, combined pairwise, and the wave's lanes are
 // summed by a fixed butterfly.
+// One token's logit of expert ei by one wave: lane sums over the row pieces
+// lane, lane + 64, ... in order (eight requested at a time; a piece index past
+// the row re-reads the last piece and is not added), then a fixed butterfly.
+__device__ __forceinline__ float router_dot1(const float* __restrict__ wr, int64_t h,
+                                             const float* __restrict__ x, int64_t ei, int lane) {
+    const float4* w4 = reinterpret_cast<const float4*>(wr + ei * h);
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const int64_t h4 = h / 4;
+    constexpr int kU = 8;
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i0 = lane; i0 < h4; i0 += 64 * kU) {
+        float4 a[kU], b[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = min(i0 + 64 * u, h4 - 1);
+            a[u] = w4[i];
+            b[u] = x4[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (i0 + 64 * u < h4) {
+                p[0] += a[u].x * b[u].x;
+                p[1] += a[u].y * b[u].y;
+                p[2] += a[u].z * b[u].z;
+                p[3] += a[u].w * b[u].w;
+            }
+        }
+    }
+    return wave_sum((p[0] + p[1]) + (p[2] + p[3]));
+}
+
 template <int kTok>
 __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restrict__ wr,
                                                             int64_t e, int64_t h,
@@ -52,17 +83,22 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
     const int lane = threadIdx.x & 63;
     const int64_t ei = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (ei >= e) return;
+    if constexpr (kTok == 1) {
+        const float sum = router_dot1(wr, h, x, ei, lane);
+        if (lane == 0) logits[ei] = sum;
+        return;
+    }
     const float4* w4 = reinterpret_cast<const float4*>(wr + ei * h);
     const int64_t h4 = h / 4;
     // token groups of kTok are spread over blockIdx.y (and looped beyond that)
     for (int64_t t0 = (int64_t)blockIdx.y * kTok; t0 < t; t0 += (int64_t)gridDim.y * kTok) {
-        const int nt = kTok == 1 ? 1 : (int)(t - t0 < kTok ? t - t0 : kTok);
+        const int nt = (int)(t - t0 < kTok ? t - t0 : kTok);
         float p[kTok][4];
 #pragma unroll
         for (int j = 0; j < kTok; ++j) p[j][0] = p[j][1] = p[j][2] = p[j][3] = 0.f;
         // pieces lane, lane + 64, ... in order; kU of them requested at a time
         // (a piece index past the row re-reads the last piece and is not added)
-        constexpr int kU = kTok == 1 ? 8 : 4;
+        constexpr int kU = 4;
         for (int64_t i0 = lane; i0 < h4; i0 += 64 * kU) {
             float4 a[kU], b[kU][kTok];
 #pragma unroll
@@ -192,20 +228,26 @@ __device__ __forceinline__ int ballot_count(bool c) {
     return __builtin_popcountll(__ballot(c));
 }
 
-template <int kPer>
-__global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restrict__ logits,
-                                                          int64_t e, int top_k,
-                                                          int32_t* __restrict__ idx,
-                                                          float* __restrict__ probs) {
-    const int64_t ti = blockIdx.x;
-    const int lane = threadIdx.x;
-    const float* l = logits + ti * e;
+// Top-k of one token's E logits (read through `load(i)`) by one wave: the
+// experts in rank order go to sel[0 .. top_k) and their renormalised
+// probabilities to selp[], both in LDS.  The wave reads back only its own LDS
+// writes (LDS operations of a wave complete in issue order, so only the
+// compiler must keep the reads after the writes).
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int kPer, typename Load>
+__device__ __forceinline__ void topk_wave(Load load, int64_t e, int top_k, int lane, int* sel,
+                                          float* selp) {
     float v[kPer];
     uint32_t key[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int64_t i = (int64_t)j * 64 + lane;
-        v[j] = i < e ? l[i] : -__builtin_inff();
+        v[j] = i < e ? load(i) : -__builtin_inff();
         key[j] = i < e ? order_key(v[j]) : 0u;   // padding ranks below every logit
     }
     // threshold = key of the top_k-th entry; `want` = how many entries equal to
@@ -226,7 +268,6 @@ __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restric
     __shared__ int cidx[kMaxTopK];
     __shared__ uint32_t ckey[kMaxTopK];
     __shared__ float cval[kMaxTopK];
-    __shared__ int sel[kMaxTopK];
     __shared__ float selv[kMaxTopK];
     int base = 0, eq_before = 0;
 #pragma unroll
@@ -245,7 +286,7 @@ __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restric
         base += __builtin_popcountll(tm);
         eq_before += __builtin_popcountll(eqm);
     }
-    __syncthreads();
+    wave_lds_order();
     // rank of entry `lane` among the selected: entries with a larger key, or an
     // equal key and a lower index, come first
     if (lane < top_k) {
@@ -257,7 +298,7 @@ __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restric
         sel[rank] = mi;
         selv[rank] = cval[lane];
     }
-    __syncthreads();
+    wave_lds_order();
     if (lane == 0) {
         float mx = selv[0];
         float ex[kMaxTopK];
@@ -266,11 +307,64 @@ __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restric
             ex[s] = expf(selv[s] - mx);
             z += ex[s];
         }
-        for (int s = 0; s < top_k; ++s) {
-            idx[ti * top_k + s] = sel[s];
-            probs[ti * top_k + s] = ex[s] / z;
-        }
+        for (int s = 0; s < top_k; ++s) selp[s] = ex[s] / z;
     }
+    wave_lds_order();
+}
+
+template <int kPer>
+__global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restrict__ logits,
+                                                          int64_t e, int top_k,
+                                                          int32_t* __restrict__ idx,
+                                                          float* __restrict__ probs) {
+    __shared__ int sel[kMaxTopK];
+    __shared__ float selp[kMaxTopK];
+    const int64_t ti = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float* l = logits + ti * e;
+    topk_wave<kPer>([&](int64_t i) { return l[i]; }, e, top_k, lane, sel, selp);
+    if (lane < top_k) {
+        idx[ti * top_k + lane] = sel[lane];
+        probs[ti * top_k + lane] = selp[lane];
+    }
+}
+
+// One token: the router and the selection in one launch.  Each wave computes
+// one expert's logit as router_logits_kernel does and stores it with a
+// device-coherent store; the workgroups count themselves on a counter in the
+// caller's control block, and the last one to finish runs the selection of
+// topk_softmax_kernel on the stored logits and returns the counter to zero.
+// The same results as the two kernels, bit for bit.
+template <int kPer>
+__global__ __launch_bounds__(256) void route1_kernel(const float* __restrict__ wr, int64_t e,
+                                                     int64_t h, const float* __restrict__ x,
+                                                     int top_k, float* __restrict__ logits,
+                                                     int32_t* __restrict__ idx,
+                                                     float* __restrict__ probs, uint32_t* ctr) {
+    __shared__ int sel[kMaxTopK];
+    __shared__ float selp[kMaxTopK];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t ei = (int64_t)blockIdx.x * 4 + (tid >> 6);
+    if (ei < e) {
+        const float sum = router_dot1(wr, h, x, ei, lane);
+        if (lane == 0) __hip_atomic_store(logits + ei, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's logit is stored
+    __syncthreads();
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 gridDim.x - 1;
+    __syncthreads();
+    if (!s_last || tid >= 64) return;
+    topk_wave<kPer>([&](int64_t i) {
+        return __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }, e, top_k, lane, sel, selp);
+    if (lane < top_k) {
+        idx[lane] = sel[lane];
+        probs[lane] = selp[lane];
+    }
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- layout ----
@@ -1624,6 +1718,37 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
                   : launch_experts_mfma<kQ8_0>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
     if (err != hipSuccess) return err;
     return launch_combine(m.dbuf, idx, probs, e, h, t, top_k, y, s);
+}
+
+size_t moe_layer_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
+    return kCtrlBytes + moe_ws_bytes(e, t, top_k, h, f);
+}
+
+hipError_t launch_moe_layer(int type, const float* wr, const uint8_t* wg, const uint8_t* wu,
+                            const uint8_t* wd, int64_t e, int64_t h, int64_t f, const float* x,
+                            int64_t t, int top_k, float* logits, int32_t* idx, float* probs,
+                            float* y, void* ws, hipStream_t s) {
+    uint8_t* mws = static_cast<uint8_t*>(ws) + kCtrlBytes;
+    hipError_t err = hipSuccess;
+    if (t == 1) {
+        // router and selection in one launch (the counter: word 0 of the control block)
+        uint32_t* ctr = static_cast<uint32_t*>(ws);
+        const dim3 grid((unsigned)((e + 3) / 4));
+        if (e <= 128)
+            hipLaunchKernelGGL((route1_kernel<2>), grid, dim3(256), 0, s, wr, e, h, x, top_k, logits,
+                               idx, probs, ctr);
+        else if (e <= 256)
+            hipLaunchKernelGGL((route1_kernel<4>), grid, dim3(256), 0, s, wr, e, h, x, top_k, logits,
+                               idx, probs, ctr);
+        else
+            hipLaunchKernelGGL((route1_kernel<16>), grid, dim3(256), 0, s, wr, e, h, x, top_k,
+                               logits, idx, probs, ctr);
+        err = hipGetLastError();
+    } else {
+        err = launch_route(wr, e, h, x, t, top_k, idx, probs, logits, s);
+    }
+    if (err != hipSuccess) return err;
+    return launch_moe(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y, mws, s);
 }
 
 }  // namespace ggq

@@ -222,6 +222,33 @@ def test_moe_validation(g):
     assert call(tt=65536, k=1, h=16384) == ARG
 
 
+def test_moe_layer_validation(g):
+    L = g._lib
+    need = L.moe_layer_workspace_size(128, 1, 8, 2048, 768)
+    assert need == g.CTRL_BYTES + L.moe_workspace_size(128, 1, 8, 2048, 768)
+    assert L.moe_layer_workspace_size(0, 1, 8, 2048, 768) == 0
+    assert L.moe_layer_workspace_size(128, 1, 33, 2048, 768) == 0
+
+    def call(t=12, e=128, h=2048, f=768, tt=1, k=8, ws=D16, wsb=need, x=B16, wr=A16, lg=C16):
+        return L.moe_layer_gemv(t, wr, A16, A16, A16, e, h, f, x, tt, k, lg, C16, C16, C16, ws,
+                                wsb, None)
+
+    # (only failing variants are called: a valid call would launch kernels on fake pointers)
+    assert call(t=5) == UNSUP
+    assert call(h=2000) == ARG
+    assert call(k=9, e=8) == ARG
+    assert call(k=33) == ARG
+    assert call(e=1025) == ARG
+    assert call(wr=None) == ARG
+    assert call(lg=None) == ARG
+    assert call(wr=A16 + 4) == ALIGN
+    assert call(x=B16 + 8) == ALIGN
+    assert call(wsb=need - 1) == WS
+    assert call(ws=None) == WS
+    assert call(ws=D16 + 64) == ALIGN
+    assert call(tt=0, wsb=0, ws=None) == OK
+
+
 def test_moe_gemm_validation(g):
     L = g._lib
     need = L.moe_gemm_workspace_size(128, 512, 8, 2048, 768)
