@@ -37,7 +37,7 @@ def _run(cmd):
     return err
 
 
-# Per-source flags.  The decode GEMV keeps MFMA results in ordinary VGPRs: its
+# Per-source flags.  The decode GEMVs keep MFMA results in ordinary VGPRs: their
 # few accumulators are rescaled by the vector units after every block, and with
 # AGPR results each rescale first needed a v_accvgpr_read.  It also asks a work
 # counter with one atomic from one lane while the next unit's loads are in
@@ -47,6 +47,7 @@ def _run(cmd):
 FILE_FLAGS = {
     "gemv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
                       "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+    "gemv_ks.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

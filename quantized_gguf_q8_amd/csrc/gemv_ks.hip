@@ -16,7 +16,12 @@
 //     exact fp16 (hi, lo) pairs in its own LDS region: each batch row b is
 //     scaled by a power of two 2^S_b from the largest |x| of the wave's 256
 //     columns (so the largest lands in [2^14, 2^15)), hi = fp16(x'),
-//     lo = fp16(x' - hi); no other wave reads them, so no barrier is needed,
+//     lo = fp16(x' - hi); no other wave reads them, so no barrier is needed.
+//     Q4_K launches of more workgroups than compute units split first and
+//     issue the weight loads after: a compute unit returns loads in the order
+//     they were issued, so activation loads issued behind a full chip's weight
+//     requests wait for them (measured: 9.6 against 10.1 us for 9728 x 2560 at
+//     batch 4; Q8_0 and one-round launches lose 0.3-0.6 us the same way),
 //  3. the products: v_mfma_f32_16x16x32_f16, A = activation pairs (rows 2b: hi,
 //     2b+1: lo), B = the decoded weights (Q8_0: q, scaled by d per 32-column
 //     block; Q4_K: sc*q <= 945, exact in fp16, scaled by d per super-block, the
@@ -349,7 +354,7 @@ __device__ __forceinline__ void ks_products(const uint8_t* ureg, const KsRaw<FMT
     }
 }
 
-template <int FMT, int MT, int T>
+template <int FMT, int MT, int T, bool PF>
 __global__ __launch_bounds__(256) void gemv_ks_kernel(const KsArgs a) {
     using C = KsCfg<FMT, MT, T>;
     extern __shared__ __align__(16) uint8_t lds[];
@@ -366,15 +371,16 @@ __global__ __launch_bounds__(256) void gemv_ks_kernel(const KsArgs a) {
     uint8_t* ureg = lds + wave * C::UNIT;
 
     // 1. the wave's activation slice (cache-resident), then its weight bytes,
-    //    all requested before any arithmetic
+    //    all requested before any arithmetic (PF: the split of step 2 first)
     uint4 xr[4 * MT][2];
     ks_load_x<MT>(a, unit * kKsUnit, lane, xr);
+    float rmax[4 * MT][2];
+    if constexpr (PF) ks_prep_x<FMT, MT>(xr, ureg, lane, rmax);
     KsRaw<FMT> raw[T];
     ks_load_w<FMT, T>(a, r0, unit, live, j, h, raw);
     __builtin_amdgcn_sched_barrier(0);
     // 2. activation pairs of the wave's unit
-    float rmax[4 * MT][2];
-    ks_prep_x<FMT, MT>(xr, ureg, lane, rmax);
+    if constexpr (!PF) ks_prep_x<FMT, MT>(xr, ureg, lane, rmax);
     // 3. products of this wave's unit
     f32x4 acc[T][MT];
 #pragma unroll
@@ -513,8 +519,13 @@ int ks_cus() {
 template <int FMT, int MT, int T>
 hipError_t ks_launch(KsArgs& a, hipStream_t s) {
     using C = KsCfg<FMT, MT, T>;
-    hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, T>), dim3((unsigned)(a.tiles * a.parts)), dim3(256),
-                       C::kLds, s, a);
+    const int64_t wgs = (int64_t)a.tiles * a.parts;
+    if (FMT == kQ4_K && wgs > ks_cus())
+        hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, T, true>), dim3((unsigned)wgs), dim3(256),
+                           C::kLds, s, a);
+    else
+        hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, T, false>), dim3((unsigned)wgs), dim3(256),
+                           C::kLds, s, a);
     return hipGetLastError();
 }
 
