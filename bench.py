@@ -366,10 +366,11 @@ def secondary(g, torch, synth, only=None):
             wd = torch.from_numpy(w).to(dev)
             cps = [wd.clone() for _ in range(copies)]
             for b in (1, 4, 16):
+                # with a workspace every batch takes the single-launch
+                # matrix-core kernel (batch 1 included, at these sizes)
                 x = torch.from_numpy(synth.normal_f32((b, k), 0, synth.tid(2, n, k) + 1)).to(dev)
                 y = torch.empty((b, n), dtype=torch.float32, device=dev)
-                calls = [g.GemvGroup(g.Q4_K, [(c, n, k, x, y)], ws=None if b == 1 else "auto")
-                         for c in cps]
+                calls = [g.GemvGroup(g.Q4_K, [(c, n, k, x, y)], ws="auto") for c in cps]
                 per = 16
                 fns = [(lambda j0: (lambda: [calls[(j0 + j) % copies]() for j in range(per)]))(j0)
                        for j0 in range(0, copies, per)]

@@ -117,7 +117,10 @@ int quant_dequantize(int type, const void *w, int64_t n, int64_t k, float *out, 
  *         the matrix cores (fp32 accumulation): for one matrix, when the
  *         workspace also holds the K-part sums (quant_gemv_split_workspace_size),
  *         in a single launch that splits the activations itself; otherwise
- *         (batch >= 2) after a pass that splits them.  With NULL every batch row
+ *         (batch >= 2) after a pass that splits them.  At batch 1 only that
+ *         single launch uses the workspace, and only for Q4_K matrices that
+ *         take more workgroups than the device has compute units; other
+ *         batch-1 calls run on the vector units.  With NULL every batch row
  *         costs one fp32 FMA per weight on the vector units.  All paths meet the
  *         same tolerance.
  * A matrix may hold at most 4 GiB ((N + 64) * row bytes < 2^32) and an activation

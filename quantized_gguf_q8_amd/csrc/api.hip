@@ -110,10 +110,11 @@ static int run_gemv(int type, const ggq_gemv_desc* d, int count, int batch, void
         if (!aligned(ws, 256)) return GGQ_ERR_ALIGN;
         if (ws_bytes < gemv_ws_need(type, d, count, batch)) return GGQ_ERR_WORKSPACE;
         // one matrix, batch >= 2: a single launch with the activation split done
-        // in-kernel (at batch 1 the vector units' streaming kernel is faster)
+        // in-kernel (at batch 1 the vector units' streaming kernel is faster,
+        // except on Q4_K matrices of more than one round of workgroups)
         ggq::GemvKsPlan plan;
-        if (count == 1 && batch >= 2 &&
-            ggq::gemv_ks_plan(type, d[0].n, d[0].k, batch, ws_bytes, plan))
+        if (count == 1 && ggq::gemv_ks_plan(type, d[0].n, d[0].k, batch, ws_bytes, plan) &&
+            (batch >= 2 || plan.b1))
             return launched(ggq::launch_gemv_ks(type, d[0], batch, plan, ws, as_stream(stream)));
         const bool parts = ws_bytes >= gemv_split_need(type, d, count, batch);
         if (mfma_ok(type, d, count, batch))

@@ -39,6 +39,7 @@ hipError_t launch_gemv(int type, const uint8_t* w, int64_t n, int64_t k, const f
 struct GemvKsPlan {
     int t, mt, tiles, parts;
     size_t ws_bytes;   // workspace the plan needs (0 without K parts)
+    bool b1;           // also faster than the vector-unit kernel at batch 1
 };
 bool gemv_ks_plan(int type, int64_t n, int64_t k, int batch, size_t ws_bytes, GemvKsPlan& p);
 size_t gemv_ks_ws_bytes(int type, int64_t n, int64_t k, int batch);

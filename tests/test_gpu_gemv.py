@@ -150,6 +150,7 @@ def test_gemv_split_workspace(g, fmt, n, k, b):
 @pytest.mark.parametrize("fmt,n,k,b", [
     (Q4, 2560, 9728, 16), (Q4, 9728, 2560, 4), (Q8, 1024, 1024, 1), (Q8, 300, 6144, 9),
     (Q4, 33, 20480, 2),      # 20 K parts on 3 row tiles, ragged last tile
+    (Q4, 2560, 9728, 1),     # batch 1 on the single launch (large Q4_K)
 ])
 def test_gemv_single_launch_workspace_and_graph_replays(g, fmt, n, k, b):
     """The one-launch matrix-core GEMV of a single matrix: its K parts are added
