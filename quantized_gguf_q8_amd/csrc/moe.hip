@@ -1134,6 +1134,309 @@ __global__ __launch_bounds__(256) void moe_mfma_kernel(const MoeMfma st) {
     }
 }
 
+// Q4_K gate/up weights streamed line by line.  A row of K = 2048 weights is
+// eight 144-byte super-blocks in nine 128-byte lines, and super-block c lies
+// in lines c and c + 1 (lines 9 (c / 8) + c % 8 and the next for longer rows),
+// so after the first super-block of each eight a row needs one new line per
+// chunk.  Whole 144-byte chunks read with streaming loads fetched the line two
+// chunks share twice (1.56x the algorithmic bytes at 16 tokens); here every
+// line is read once.  The lines of a row sit in a three-slot ring in LDS, slot
+// = the workgroup's running line count mod 3: the next chunk's new line goes
+// to the slot the current chunk does not read, and when the next chunk needs
+// two new lines the second is stored after a further barrier, once the
+// current chunk's first line is no longer read.  Used when K is a multiple of
+// 2048 and the matrices start on 128-byte boundaries (every row then does too).
+template <int NMAT>
+struct MoeRingCfg {
+    // the piece map below covers 32 rows of each of two matrices
+    static_assert(NMAT == 2, "gate and up");
+    using C = MCfg<kQ4_K, 1, 4, 256>;
+    static constexpr int RPM = 64 / NMAT;
+    // 100 dwords per row: the 16 rows a wave reads start on distinct
+    // multiples of 4 banks
+    static constexpr int RS = 3 * 128 + 16;
+    static constexpr int kRing = 64 * RS;
+    // min-term operands of lane groups 0, 1 only (groups 2, 3 are zero)
+    static constexpr int kMins = 32 * 8;
+    static constexpr int kInvOff = C::kFrag + kMins;
+    static constexpr int kXBuf = kInvOff + 32;
+    // the up-to-gate hand-off at a tile's end uses the idle activation buffer
+    static_assert(2 * 64 * 2 * 4 <= kXBuf, "hand-off fits an activation buffer");
+    static constexpr int kLds = kRing + 2 * kXBuf;
+    static constexpr int FPIECES = C::kFrag / 16;
+    static constexpr int FP = (FPIECES + 255) / 256;
+    static constexpr int MPIECES = kMins / 8;
+    static constexpr int MP = (MPIECES + 255) / 256;
+};
+
+template <int NMAT>
+struct MoeRingPrefetch {
+    using R = MoeRingCfg<NMAT>;
+    using C = typename R::C;
+    uint4 w[4];         // 64 rows x up to two lines x 8 pieces = 1024 pieces
+    uint4 f[R::FP];
+    uint2 mn[R::MP];
+    float inv;
+    int ibatch;
+    uint32_t wst;       // bit i: piece i is stored
+    uint32_t wzero;     // bit i: ... as zeros (row past the matrix)
+    uint32_t wlate;     // bit i: ... after the current chunk's reads (second of two new lines)
+    uint32_t wdst[4];   // ring byte offset of piece i
+
+    // g: ring position of the unit's first line of this chunk.
+    template <bool LDSL>
+    __device__ __forceinline__ void load(const MoeMfma& st, const MoeUnit& u, int g, int tid) {
+        const int cp = u.chunk & 7;
+        const bool two = cp == 0;   // first chunk of eight: both of its lines are new
+        const uint32_t l0 = 9u * (uint32_t)(u.chunk >> 3) + (uint32_t)cp;
+        const uint32_t bytes = (uint32_t)(st.n * st.rb);
+        const __amdgpu_buffer_rsrc_t r0 =
+            make_rsrc_uniform(st.w[0] + (int64_t)u.e * st.n * st.rb, bytes);
+        const __amdgpu_buffer_rsrc_t r1 =
+            make_rsrc_uniform(st.w[NMAT - 1] + (int64_t)u.e * st.n * st.rb, bytes);
+        const uint32_t rb = (uint32_t)st.rb;
+        wst = 0;
+        wzero = 0;
+        wlate = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + 256 * i;
+            // two lines: q = (matrix, row, line, piece); one line: (matrix, row,
+            // piece) and pieces 2, 3 idle.  The matrix is uniform per i.
+            const int m = two ? i >> 1 : i;
+            const int r = two ? (q & 511) >> 4 : (q & 255) >> 3;
+            const int line = two ? (q >> 3) & 1 : 1;
+            const int byte = (q & 7) * 16;
+            const bool live = m < NMAT;
+            const uint32_t row = (uint32_t)u.r0 + (uint32_t)r;
+            const bool in = live && row < (uint32_t)st.n;
+            w[i] = buf_load16<true>(m == 1 ? r1 : r0, in ? row * rb + (l0 + line) * 128 + byte : kOob);
+            wst |= (uint32_t)live << i;
+            wzero |= (uint32_t)(live && !in) << i;
+            wlate |= (uint32_t)(live && two && line == 1) << i;
+            wdst[i] = (uint32_t)((m * R::RPM + r) * R::RS + ((g + line) % 3) * 128 + byte);
+        }
+        const int batch = min(8, u.cnt - u.g0);
+        const XfLayout L = xf_layout(kQ4_K, st.k, st.xmt);
+        const __amdgpu_buffer_rsrc_t rf = make_rsrc(st.xf, (uint32_t)L.bytes);
+        const int nblk = st.k / 32, nsb = st.k / 256;
+#pragma unroll
+        for (int i = 0; i < R::FP; ++i) {
+            const int q = tid + 256 * i;
+            const int blk = q / 64, l = q % 64;
+            const int sl = (l & 15) >> 1;
+            uint32_t off = kOob;
+            const int kb = u.chunk * C::NBLK + blk;
+            if (q < R::FPIECES && sl < batch && kb < nblk) {
+                const int row = u.xrows ? lget<LDSL>(u.xrows, u.g0 + sl) : lget<LDSL>(u.pairs, u.g0 + sl) / st.xdiv;
+                const int sln = 2 * (row & 7) + (l & 1) + 16 * (l >> 4);
+                off = (uint32_t)(L.frag + (((int64_t)(row >> 3) * nblk + kb) * 64 + sln) * 16);
+            }
+            f[i] = buf_load16<false>(rf, off);
+        }
+#pragma unroll
+        for (int i = 0; i < R::MP; ++i) {
+            const int q = tid + 256 * i;
+            const int sb = q / 64, l = q % 64;
+            const int sl = (l & 15) >> 1;
+            const int ksb = u.chunk + sb;
+            uint32_t off = kOob;
+            if (q < R::MPIECES && sl < batch && ksb < nsb) {
+                const int row = u.xrows ? lget<LDSL>(u.xrows, u.g0 + sl) : lget<LDSL>(u.pairs, u.g0 + sl) / st.xdiv;
+                const int sln = 2 * (row & 7) + (l & 1) + 16 * (l >> 4);
+                off = (uint32_t)(L.mins + (((int64_t)(row >> 3) * nsb + ksb) * 64 + sln) * 8);
+            }
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rf, off, 0, 0);
+            mn[i] = make_uint2(v.x, v.y);
+        }
+        ibatch = batch;
+        if (tid < 8) {
+            const int t = tid < batch ? tid : 0;
+            const int row = u.xrows ? lget<LDSL>(u.xrows, u.g0 + t) : lget<LDSL>(u.pairs, u.g0 + t) / st.xdiv;
+            inv = __builtin_bit_cast(float,
+                                     __builtin_amdgcn_raw_buffer_load_b32(rf, (uint32_t)(L.inv + 4 * row), 0, 0));
+        }
+    }
+
+    // Everything but the late pieces (store_late, after a barrier).
+    __device__ __forceinline__ void store(uint8_t* ring, uint8_t* xb, int tid) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (((wst & ~wlate) >> i) & 1u)
+                *reinterpret_cast<uint4*>(ring + wdst[i]) = (wzero >> i) & 1u ? make_uint4(0, 0, 0, 0) : w[i];
+#pragma unroll
+        for (int i = 0; i < R::FP; ++i) {
+            const int q = tid + 256 * i;
+            if (q < R::FPIECES) *reinterpret_cast<uint4*>(xb + q * 16) = f[i];
+        }
+#pragma unroll
+        for (int i = 0; i < R::MP; ++i) {
+            const int q = tid + 256 * i;
+            if (q < R::MPIECES) *reinterpret_cast<uint2*>(xb + C::kFrag + q * 8) = mn[i];
+        }
+        if (tid < 8) reinterpret_cast<float*>(xb + R::kInvOff)[tid] = tid < ibatch ? inv : 1.f;
+    }
+
+    __device__ __forceinline__ void store_late(uint8_t* ring) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if ((wlate >> i) & 1u)
+                *reinterpret_cast<uint4*>(ring + wdst[i]) = (wzero >> i) & 1u ? make_uint4(0, 0, 0, 0) : w[i];
+    }
+};
+
+// The products of one super-block (chunk) from the ring: the Q4_K arithmetic
+// of mfma_chunk (gemv_mfma_core.h) for one 16-row group, with the bytes read
+// from the two ring slots that hold the super-block.
+template <int NMAT>
+__device__ __forceinline__ void ring_chunk(const uint8_t* ring, const uint8_t* xb, int g, int cp,
+                                           int lane, int wave, int j, int h, f32x4& acc) {
+    using R = MoeRingCfg<NMAT>;
+    using C = typename R::C;
+    const uint8_t* rowp = ring + (16 * wave + j) * R::RS;
+    const uint8_t* b0 = rowp + (g % 3) * 128;
+    const uint8_t* b1 = rowp + ((g + 1) % 3) * 128;
+    const int s0 = 16 * cp;   // super-block start inside its first line
+    // every LDS read of the chunk first, then the arithmetic
+    const uint4 hd = *reinterpret_cast<const uint4*>(b0 + s0);
+    uint2 qv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int x = s0 + 16 + 32 * c + 8 * h;   // 8-byte pieces never straddle a line
+        qv[c] = *reinterpret_cast<const uint2*>(x < 128 ? b0 + x : b1 + (x - 128));
+    }
+    f16x8 aop[8];
+#pragma unroll
+    for (int sub = 0; sub < 8; ++sub)
+        aop[sub] = *reinterpret_cast<const f16x8*>(xb + sub * 1024 + lane * 16);
+    const f16x4 xop = h < 2 ? *reinterpret_cast<const f16x4*>(xb + C::kFrag + lane * 8)
+                            : f16x4{0, 0, 0, 0};
+    const float d = half_bits_to_float(hd.x);
+    const float dmin = half_bits_to_float(hd.x >> 16);
+    const Q4KScales scl = q4k_unpack(hd.y, hd.z, hd.w);
+    f32x4 dsb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+            const int sub = 2 * c + hi;
+            uint32_t scj, mj;
+            q4k_sub(scl, sub, scj, mj);
+            const _Float16 sch = (_Float16)(float)scj;
+            const _Float16 msch = (_Float16)(-1024.f * (float)scj);
+            const f16x2 sc2 = {sch, sch};
+            const f16x2 msc2 = {msch, msch};
+            const uint32_t n0 = hi ? (qv[c].x >> 4) & 0x0F0F0F0Fu : qv[c].x & 0x0F0F0F0Fu;
+            const uint32_t n1 = hi ? (qv[c].y >> 4) & 0x0F0F0F0Fu : qv[c].y & 0x0F0F0F0Fu;
+            uint32_t b4[4];
+            q4x4_to_f16(n0, sc2, msc2, b4[0], b4[1]);
+            q4x4_to_f16(n1, sc2, msc2, b4[2], b4[3]);
+            const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(b4[0], b4[1], b4[2], b4[3]));
+            dsb = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[sub], bop, dsb, 0, 0, 0);
+        }
+    }
+    // min term: B[k][col] = m_k of this row for k < 8, zero above
+    const uint32_t mv = h == 0 ? scl.mnl : scl.mnh;
+    uint32_t m0 = 0, m1 = 0;
+    if (h < 2) {
+        const uint32_t e = 0x64646464u;
+        const f16x2 off = {(_Float16)1024.f, (_Float16)1024.f};
+        m0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(e, mv, 0x04010400u)) - off);
+        m1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(e, mv, 0x04030402u)) - off);
+    }
+    const f16x4 mop = __builtin_bit_cast(f16x4, make_uint2(m0, m1));
+    const f32x4 dmn = __builtin_amdgcn_mfma_f32_16x16x16f16(xop, mop, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    acc += d * dsb - (32.f * dmin) * dmn;
+}
+
+// moe_mfma_kernel for Q4_K with the weights in line rings (see MoeRingCfg).
+template <int NMAT, bool LDSL>
+__global__ __launch_bounds__(256) void moe_ring_kernel(const MoeMfma st) {
+    using R = MoeRingCfg<NMAT>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;
+    const int h = lane >> 4;
+    uint8_t* ring = lds;
+    uint8_t* xbufs = lds + R::kRing;
+
+    MoeLists L;
+    if constexpr (LDSL) {
+        L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lds + R::kLds));
+    } else {
+        L = MoeLists{st.ws.cnt, st.ws.off, st.ws.active, st.ws.list, nullptr, st.ws.nact[0]};
+    }
+    const int total = L.nact * st.tiles;
+
+    MoeStage ms{};
+    ms.nchunk = st.nchunk;
+    ms.tiles = st.tiles;
+    MoeUnit cur;
+    if (!moe_locate<R::RPM, LDSL>(ms, L, blockIdx.x, total, cur)) return;
+    int g = 0;   // ring position of the current chunk's first line
+    MoeRingPrefetch<NMAT> pf;
+    pf.template load<LDSL>(st, cur, g, tid);
+    pf.store(ring, xbufs, tid);
+    pf.store_late(ring);
+    __syncthreads();
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    int buf = 0;
+    for (;;) {
+        MoeUnit nxt;
+        const bool more = moe_next<8, R::RPM, LDSL>(ms, L, cur, total, nxt);
+        const int gn = g + ((nxt.chunk & 7) == 0 ? 2 : 1);
+        // unconditional (the last unit reloads itself, never stored)
+        pf.template load<LDSL>(st, more ? nxt : cur, more ? gn : g, tid);
+        const uint8_t* xb = xbufs + buf * R::kXBuf;
+        ring_chunk<NMAT>(ring, xb, g, cur.chunk & 7, lane, wave, j, h, acc);
+        if (cur.chunk == st.nchunk - 1) {
+            const float* invb = reinterpret_cast<const float*>(xb + R::kInvOff);
+            const int batch = min(8, cur.cnt - cur.g0);
+            const int br = 16 * wave + j;
+            const int64_t r = cur.r0 + br % R::RPM;
+            const float v0 = (acc[0] + acc[1]) * invb[2 * h];
+            const float v1 = (acc[2] + acc[3]) * invb[2 * h + 1];
+            if constexpr (NMAT == 2) {
+                // up rows (waves 2, 3) hand their values to the gate rows (waves 0, 1)
+                float* red = reinterpret_cast<float*>(xbufs + (buf ^ 1) * R::kXBuf);
+                if (wave >= 2) {
+                    red[((wave - 2) * 64 + lane) * 2] = v0;
+                    red[((wave - 2) * 64 + lane) * 2 + 1] = v1;
+                }
+                __syncthreads();
+                if (wave < 2 && r < st.n) {
+                    const float u0 = red[(wave * 64 + lane) * 2], u1 = red[(wave * 64 + lane) * 2 + 1];
+                    if (2 * h < batch)
+                        st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h) * st.ldy + r] = v0 / (1.0f + expf(-v0)) * u0;
+                    if (2 * h + 1 < batch)
+                        st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h + 1) * st.ldy + r] = v1 / (1.0f + expf(-v1)) * u1;
+                }
+                __syncthreads();
+            } else {
+                if (r < st.n) {
+                    if (2 * h < batch) st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h) * st.ldy + r] = v0;
+                    if (2 * h + 1 < batch) st.y[(int64_t)lget<LDSL>(cur.pairs, cur.g0 + 2 * h + 1) * st.ldy + r] = v1;
+                }
+            }
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (!more) break;
+        buf ^= 1;
+        pf.store(ring, xbufs + buf * R::kXBuf, tid);
+        __syncthreads();
+        if ((nxt.chunk & 7) == 0) {   // two new lines: the second replaces this chunk's first
+            pf.store_late(ring);
+            __syncthreads();
+        }
+        cur = nxt;
+        g = gn;
+    }
+}
+
 // y[t][r] = sum_s probs[t][s] * d[(t*top_k + s)][r], slot order.  Pairs whose
 // expert index is out of range were grouped with expert 0 and carry whatever
 // its matrices gave; their term is skipped (not multiplied by 0), so a
@@ -1436,8 +1739,41 @@ hipError_t launch_mstage_l(MoeMfma st, int64_t slots, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int NMAT, bool LDSL>
+hipError_t launch_ring_l(MoeMfma st, int64_t slots, hipStream_t s) {
+    using R = MoeRingCfg<NMAT>;
+    const size_t lds = R::kLds + (LDSL ? inline_group_bytes(st.e, st.p) : 0);
+    static size_t per_cu_lds = 0;
+    static int per_cu = 0;
+    if (per_cu_lds != lds) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(moe_ring_kernel<NMAT, LDSL>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe_ring_kernel<NMAT, LDSL>, 256, lds) !=
+                hipSuccess ||
+            v <= 0)
+            v = 1;
+        per_cu = v;
+        per_cu_lds = lds;
+    }
+    st.nchunk = st.k / 256;
+    st.tiles = (int32_t)((st.n + R::RPM - 1) / R::RPM);
+    const int64_t most = slots * st.tiles;
+    const int64_t cap = (int64_t)per_cu * moe_device_cus();
+    const unsigned grid = (unsigned)(most < cap ? most : cap);
+    hipLaunchKernelGGL((moe_ring_kernel<NMAT, LDSL>), dim3(grid), dim3(256), lds, s, st);
+    return hipGetLastError();
+}
+
 template <int FMT, int NMAT>
 hipError_t launch_mstage(const MoeMfma& st, int64_t slots, hipStream_t s) {
+    const bool ring = FMT == kQ4_K && NMAT == 2 && st.k % 2048 == 0 &&
+                      reinterpret_cast<uintptr_t>(st.w[0]) % 128 == 0 &&
+                      reinterpret_cast<uintptr_t>(st.w[NMAT - 1]) % 128 == 0;
+    if constexpr (NMAT == 2)
+        if (ring)
+            return st.inline_group ? launch_ring_l<NMAT, true>(st, slots, s)
+                                   : launch_ring_l<NMAT, false>(st, slots, s);
     return st.inline_group ? launch_mstage_l<FMT, NMAT, true>(st, slots, s)
                            : launch_mstage_l<FMT, NMAT, false>(st, slots, s);
 }
