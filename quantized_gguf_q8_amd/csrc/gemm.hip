@@ -173,6 +173,10 @@ __device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int g, 
         // top two bits of s[j-4], min high nibble of s[j+4] with those of s[j].
         uint32_t sc0, m0, sc1, m1;
         if (g < 2) {
+            // hdr.w is not needed here, but its register must stay this load's
+            // until the load is waited for: handed to the allocator as free, it
+            // is reused at once and the write waits for every load in flight
+            asm volatile("" : : "v"(r.hdr.w));
             const int sh = 16 * g;
             sc0 = (r.hdr.y >> sh) & 63u;
             sc1 = (r.hdr.y >> (sh + 8)) & 63u;
@@ -337,9 +341,13 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
     };
 
     if (nk > 0) {
+        // A first, as in the loop: at the loop head the A fragments are then
+        // followed by weight loads on every path into it, and the first
+        // step's wait for them need not drain the weight prefetch
+        load_a(0, af);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = 0; d < kDW; ++d) load_w(d, ru[d]);
-        load_a(0, af);
         store_w(0, ru[0], wl);
     }
     __syncthreads();
