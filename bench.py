@@ -76,12 +76,22 @@ def capture(torch, fns):
     return graphs
 
 
-def replay_ms(torch, graphs, reps, per_graph=1):
-    for i in range(min(len(graphs), 3)):
-        graphs[i].replay()
-    torch.cuda.synchronize()
+def replay_ms(torch, graphs, reps, per_graph=1, warm_ms=20.0):
+    """ms per call over `reps` replays (round robin over `graphs`, each of
+    `per_graph` calls), after about warm_ms of untimed replays: the kernels run
+    a few percent faster once the shader clock has settled under load."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    e0.record()
+    graphs[0].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    for i in range(max(len(graphs), int(warm_ms / one) + 1)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
     e0.record()
     for i in range(reps):
         graphs[i % len(graphs)].replay()
@@ -92,26 +102,18 @@ def replay_ms(torch, graphs, reps, per_graph=1):
 
 def steady_ms(torch, graph, per_graph, warm_ms=25.0, timed_ms=25.0):
     """ms per call of a graph of `per_graph` calls at steady state: replayed for
-    about warm_ms first (compute-bound kernels speed up over the first tens of
-    milliseconds as the shader clock settles), then timed over about timed_ms."""
-    graph.replay()
-    torch.cuda.synchronize()
+    about warm_ms first, then timed over about timed_ms (compute-bound kernels
+    speed up over the first tens of milliseconds as the shader clock settles)."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    graph.replay()
+    torch.cuda.synchronize()
     e0.record()
     graph.replay()
     e1.record()
     torch.cuda.synchronize()
     one = max(e0.elapsed_time(e1), 1e-3)
-    for _ in range(int(warm_ms / one) + 1):
-        graph.replay()
-    reps = int(timed_ms / one) + 1
-    e0.record()
-    for _ in range(reps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * per_graph)
+    return replay_ms(torch, [graph], int(timed_ms / one) + 1, per_graph, warm_ms)
 
 
 def main():
