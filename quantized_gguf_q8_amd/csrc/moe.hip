@@ -503,6 +503,12 @@ struct MoeStage {
                            // every pair to expert 0, the dense gated FFN)
     int32_t p, e;          // pairs, experts
     int32_t inline_group;
+    // One token, gate/up with inline grouping: when set, every workgroup selects
+    // the experts itself from the router's logits (idx is not read), and
+    // workgroup 0 stores the selection and its probabilities.
+    const float* logits;
+    int32_t* idx_out;
+    float* probs_out;
 };
 
 // Pair lists by expert: counts, list offsets, ascending active experts, and the
@@ -847,7 +853,28 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(const MoeStage st) {
     MoeLists L;
     if constexpr (LDSL) {
         uint8_t* lists = SINGLE ? lds + C::kWBytes + C::kXBuf : lds + C::kLds;
-        L = group_in_lds(st.idx, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lists));
+        const int32_t* ix = st.idx;
+        if constexpr (NB == 1 && NMAT == 2) {
+            if (st.logits) {
+                // topk_softmax_kernel's selection, in every workgroup: the
+                // logits are 4 bytes per expert, and this saves the launch
+                // that would hand the selection over
+                __shared__ int s_sel[kMaxTopK];
+                __shared__ float s_selp[kMaxTopK];
+                if (tid < 64) {
+                    auto ld = [&](int64_t i) { return st.logits[i]; };
+                    if (st.e <= 128) topk_wave<2>(ld, st.e, st.p, tid, s_sel, s_selp);
+                    else topk_wave<4>(ld, st.e, st.p, tid, s_sel, s_selp);
+                    if (blockIdx.x == 0 && tid < st.p) {
+                        st.idx_out[tid] = s_sel[tid];
+                        st.probs_out[tid] = s_selp[tid];
+                    }
+                }
+                __syncthreads();
+                ix = s_sel;
+            }
+        }
+        L = group_in_lds(ix, st.p, st.e, st.xdiv, reinterpret_cast<int32_t*>(lists));
     } else {
         L = MoeLists{st.ws.cnt, st.ws.off, st.ws.active, st.ws.list, nullptr, st.ws.nact[0]};
     }
@@ -1492,28 +1519,20 @@ struct D1Raw<kQ8_0> {
     uint32_t v[17];      // two blocks, 68 bytes
 };
 
-template <int FMT>
-__global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    float* lh = reinterpret_cast<float*>(lds);   // [top_k][F / 64][kD1Stride]
-    float* lpart = lh + a.top_k * a.upr * kD1Stride;   // one partial sum per unit
-    __shared__ int s_ex[kMaxTopK];
-    __shared__ float s_p[kMaxTopK];
-    const int tid = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+// The loads of a thread's down units (at most U): workgroup rows r0 .. r0 +
+// rows - 1, slot experts from ex_of(slot).
+template <int FMT, int U, typename ExOf>
+__device__ __forceinline__ void d1_load(const Down1Args& a, int64_t r0, int tid, ExOf ex_of,
+                                        D1Raw<FMT> (&raw)[U], bool (&live)[U]) {
     const int per_slot = a.rows * a.upr;
     const int total = a.top_k * per_slot;
-
-    // weights of this thread's units (loads first: they take longest)
-    D1Raw<FMT> raw[kD1Units];
-    bool live[kD1Units];
 #pragma unroll
-    for (int j = 0; j < kD1Units; ++j) {
+    for (int j = 0; j < U; ++j) {
         const int u = tid + 256 * j;
         const int slot = u / per_slot, rem = u % per_slot;
         const int64_t row = r0 + rem / a.upr;
         const int piece = rem % a.upr;
-        const int ex = u < total ? a.idx[slot] : -1;
+        const int ex = u < total ? ex_of(slot) : -1;
         live[j] = u < total && ex >= 0 && ex < a.e && row < a.hdim;
         if (!live[j]) continue;
         const uint8_t* rp = a.wd + ((int64_t)ex * a.hdim + row) * a.rb;
@@ -1528,22 +1547,46 @@ __global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
             for (int i = 0; i < 17; ++i) raw[j].v[i] = __builtin_nontemporal_load(q + i);
         }
     }
-    // h of every slot (rows of slots without an expert are copied too and never
-    // used), the slots' experts and weights for the final sums
-    const int hq = a.top_k * a.f / 4;
-    for (int i = tid; i < hq; i += 256) {
-        const int c = 4 * i, slot = c / a.f, col = c % a.f;
-        *reinterpret_cast<float4*>(lh + (slot * a.upr + col / 64) * kD1Stride + col % 64) =
-            reinterpret_cast<const float4*>(a.h)[i];
-    }
-    if (tid < a.top_k) {
-        s_ex[tid] = a.idx[tid];
-        s_p[tid] = a.probs[tid];
-    }
-    __syncthreads();
+}
 
+// h of every slot into LDS as [top_k][F / 64][kD1Stride] (rows of slots without
+// an expert are copied too and never used), 16 bytes per lane, eight loads per
+// lane in flight at a time (one at a time, each load is a round trip).
+constexpr int kD1HBatch = 8;
+
+__device__ __forceinline__ void d1_stage_h(const Down1Args& a, float* lh, int tid) {
+    const int hq = a.top_k * a.f / 4;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(a.h, (uint32_t)hq * 16u);
+    for (int i0 = 0; i0 < hq; i0 += 256 * kD1HBatch) {
+        u32x4 v[kD1HBatch];
 #pragma unroll
-    for (int j = 0; j < kD1Units; ++j) {
+        for (int j = 0; j < kD1HBatch; ++j) {
+            const int i = i0 + 256 * j + tid;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, i < hq ? (uint32_t)i * 16u : kOob, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kD1HBatch; ++j) {
+            const int i = i0 + 256 * j + tid;
+            if (i < hq) {
+                const int c = 4 * i, slot = c / a.f, col = c % a.f;
+                *reinterpret_cast<u32x4*>(lh + (slot * a.upr + col / 64) * kD1Stride + col % 64) = v[j];
+            }
+        }
+    }
+}
+
+// The units' partial sums, then each (slot, row) and each row in order, with
+// h staged in lh and the slots' experts and weights in s_ex / s_p (all visible
+// to every thread on entry).
+template <int FMT, int U>
+__device__ __forceinline__ void d1_finish(const Down1Args& a, int64_t r0, int tid,
+                                          const D1Raw<FMT> (&raw)[U], const bool (&live)[U],
+                                          float* lh, float* lpart, const int* s_ex,
+                                          const float* s_p) {
+    const int per_slot = a.rows * a.upr;
+    const int total = a.top_k * per_slot;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
         const int u = tid + 256 * j;
         if (u >= total) break;
         float part = 0.f;
@@ -1616,6 +1659,28 @@ __global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
         }
         a.y[r0 + tid] = acc;
     }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void moe_down1_kernel(const Down1Args a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    float* lh = reinterpret_cast<float*>(lds);   // [top_k][F / 64][kD1Stride]
+    float* lpart = lh + a.top_k * a.upr * kD1Stride;   // one partial sum per unit
+    __shared__ int s_ex[kMaxTopK];
+    __shared__ float s_p[kMaxTopK];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * a.rows;
+    // weights of this thread's units (loads first: they take longest)
+    D1Raw<FMT> raw[kD1Units];
+    bool live[kD1Units];
+    d1_load<FMT, kD1Units>(a, r0, tid, [&](int slot) { return a.idx[slot]; }, raw, live);
+    d1_stage_h(a, lh, tid);
+    if (tid < a.top_k) {
+        s_ex[tid] = a.idx[tid];
+        s_p[tid] = a.probs[tid];
+    }
+    __syncthreads();
+    d1_finish<FMT, kD1Units>(a, r0, tid, raw, live, lh, lpart, s_ex, s_p);
 }
 
 int moe_device_cus() {
@@ -1843,16 +1908,29 @@ hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8
     return launch_stage_rows<FMT, 4, 1>(d, slots, t, s);
 }
 
+// The router's logits of one token, from which the one-token gate/up stage
+// selects the experts itself (storing the selection in idx / probs).
+struct MoeSelect {
+    const float* logits;
+    int32_t* idx;
+    float* probs;
+};
+
 template <int FMT, int NB>
 hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, int64_t e,
                           int64_t hdim, int64_t f, const float* x, int64_t t, int top_k,
                           const int32_t* idx, const MoeWs& ws, hipStream_t s,
-                          bool down = true) {
+                          bool down = true, const MoeSelect* sel = nullptr) {
     const int64_t p = t * top_k;
     const int64_t slots = p < e ? p : e;
     const bool inl = p <= kInlinePairs;
     MoeStage a{};
     a.idx = idx;
+    if (sel) {
+        a.logits = sel->logits;
+        a.idx_out = sel->idx;
+        a.probs_out = sel->probs;
+    }
     a.p = (int32_t)p;
     a.e = (int32_t)e;
     a.inline_group = inl;
@@ -2066,6 +2144,21 @@ hipError_t launch_moe_layer(int type, const float* wr, const uint8_t* wg, const 
                             float* y, void* ws, hipStream_t s) {
     uint8_t* mws = static_cast<uint8_t*>(ws) + kCtrlBytes;
     hipError_t err = hipSuccess;
+    if (t == 1 && e <= 256 && down1_fits(f, top_k)) {
+        // router; gate/up, whose workgroups each take the selection from the
+        // logits (workgroup 0 stores it); down and the combine
+        hipLaunchKernelGGL((router_logits_kernel<1>), dim3((unsigned)((e + 3) / 4), 1), dim3(256), 0,
+                           s, wr, e, h, x, t, logits);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const MoeWs m = carve(mws, e, t, top_k, h, f);
+        const MoeSelect sel{logits, idx, probs};
+        err = type == kQ4_K
+                  ? launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s, false, &sel)
+                  : launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s, false, &sel);
+        if (err != hipSuccess) return err;
+        return launch_down1(type, wd, e, h, f, m.hbuf, idx, probs, top_k, y, s);
+    }
     if (t == 1) {
         // router and selection in one launch (the counter: word 0 of the control block)
         uint32_t* ctr = static_cast<uint32_t*>(ws);

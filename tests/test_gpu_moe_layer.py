@@ -1,10 +1,11 @@
 """GPU parity: moe_layer_gemv (router, selection and routed experts in one
-call; for one token the router and the selection are one launch) against
+call; for one token of at most 256 experts the gate/up stage takes the
+selection from the router's logits itself) against
 moe_route followed by moe_expert_gemv, bit for bit, and end to end against
 the CPU oracle.
 
 README opening paragraph: each token goes to a few experts and only their
-weights take part.  The one-launch routing runs the same arithmetic as the
+weights take part.  The fused routing runs the same arithmetic as the
 router and top-k kernels, so logits, indices, probabilities and y must be
 identical; the two-call path itself is checked against the oracle in
 test_gpu_moe.py.
@@ -58,6 +59,7 @@ def _same(a, b, what):
     (Q4, 128, 2048, 768, 1, 8),      # the 35B-A3B-class layer, one token
     (Q8, 128, 2048, 768, 1, 8),
     (Q8, 200, 512, 256, 1, 6),       # 4 logits per lane in the selection, E % 4 != 0
+    (Q4, 256, 1024, 512, 1, 8),      # the most experts the gate/up stage selects from
     (Q4, 1024, 256, 256, 1, 32),     # 16 logits per lane, top-32
     (Q4, 5, 1024, 512, 1, 1),        # top-1, two router workgroups (one partly idle)
     (Q4, 16, 512, 2048, 1, 8),       # down stage without the one-token kernel
