@@ -288,27 +288,29 @@ __device__ __forceinline__ void topk_wave(Load load, int64_t e, int top_k, int l
     }
     wave_lds_order();
     // rank of entry `lane` among the selected: entries with a larger key, or an
-    // equal key and a lower index, come first
+    // equal key and a lower index, come first (each selected entry broadcast
+    // from its lane)
+    const uint32_t mk = lane < top_k ? ckey[lane] : 0u;
+    const int mi = lane < top_k ? cidx[lane] : 0;
+    const float mv = lane < top_k ? cval[lane] : 0.f;
+    int rank = 0;
+    for (int q = 0; q < top_k; ++q) {
+        const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)mk, q);
+        const int iq = __builtin_amdgcn_readlane(mi, q);
+        rank += (kq > mk || (kq == mk && iq < mi)) ? 1 : 0;
+    }
     if (lane < top_k) {
-        const uint32_t mk = ckey[lane];
-        const int mi = cidx[lane];
-        int rank = 0;
-        for (int q = 0; q < top_k; ++q)
-            rank += (ckey[q] > mk || (ckey[q] == mk && cidx[q] < mi)) ? 1 : 0;
         sel[rank] = mi;
-        selv[rank] = cval[lane];
+        selv[rank] = mv;
     }
     wave_lds_order();
-    if (lane == 0) {
-        float mx = selv[0];
-        float ex[kMaxTopK];
-        float z = 0.f;
-        for (int s = 0; s < top_k; ++s) {
-            ex[s] = expf(selv[s] - mx);
-            z += ex[s];
-        }
-        for (int s = 0; s < top_k; ++s) selp[s] = ex[s] / z;
-    }
+    // softmax of the selected logits in rank order: lane s takes exp(v_s - v_0),
+    // and the normaliser adds them in rank order
+    const float ex = expf((lane < top_k ? selv[lane] : selv[0]) - selv[0]);
+    float z = 0.f;
+    for (int q = 0; q < top_k; ++q)
+        z += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), q));
+    if (lane < top_k) selp[lane] = ex / z;
     wave_lds_order();
 }
 
