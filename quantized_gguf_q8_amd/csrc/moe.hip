@@ -250,18 +250,27 @@ __device__ __forceinline__ void topk_wave(Load load, int64_t e, int top_k, int l
         v[j] = i < e ? load(i) : -__builtin_inff();
         key[j] = i < e ? order_key(v[j]) : 0u;   // padding ranks below every logit
     }
-    // threshold = key of the top_k-th entry; `want` = how many entries equal to
-    // it are taken (the lowest indices among them)
+    // threshold = the top_k-th largest key on the bits in `mask`; `want` = how
+    // many entries equal to it there are taken (the lowest indices among them).
+    // Bits are fixed from the top; once the entries that share the threshold's
+    // prefix are exactly the `want` still to take, the selection is settled and
+    // the lower bits are left out of the mask.
     uint32_t thr = 0, mask = 0;
     int want = top_k;
-    for (int bit = 31; bit >= 0; --bit) {
+    int group = kPer * 64;   // entries whose key matches thr on the mask
+    for (int bit = 31; bit >= 0 && group != want; --bit) {
         const uint32_t cand = thr | (1u << bit);
         const uint32_t m = mask | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) cnt += ballot_count((key[j] & m) == cand);
-        if (cnt >= want) thr = cand;
-        else want -= cnt;
+        if (cnt >= want) {
+            thr = cand;
+            group = cnt;
+        } else {
+            want -= cnt;
+            group -= cnt;
+        }
         mask = m;
     }
     // compact the selected entries (index order) into LDS
@@ -272,10 +281,11 @@ __device__ __forceinline__ void topk_wave(Load load, int64_t e, int top_k, int l
     int base = 0, eq_before = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const uint64_t eqm = __ballot(key[j] == thr);
+        const uint32_t km = key[j] & mask;
+        const uint64_t eqm = __ballot(km == thr);
         const uint64_t below = (1ull << lane) - 1ull;   // lanes under this one
-        const bool tie_ok = key[j] == thr && eq_before + __builtin_popcountll(eqm & below) < want;
-        const bool take = key[j] > thr || tie_ok;
+        const bool tie_ok = km == thr && eq_before + __builtin_popcountll(eqm & below) < want;
+        const bool take = km > thr || tie_ok;
         const uint64_t tm = __ballot(take);
         if (take) {
             const int pos = base + __builtin_popcountll(tm & below);
