@@ -119,8 +119,9 @@ int quant_dequantize(int type, const void *w, int64_t n, int64_t k, float *out, 
  *         in a single launch that splits the activations itself; otherwise
  *         (batch >= 2) after a pass that splits them.  At batch 1 only that
  *         single launch uses the workspace, and only for Q4_K matrices that
- *         take more workgroups than the device has compute units; other
- *         batch-1 calls run on the vector units.  With NULL every batch row
+ *         take more workgroups than the device has compute units and whose
+ *         rows are few and long (fewer than 16 per compute unit, K above
+ *         6144); other batch-1 calls run on the vector units.  With NULL every batch row
  *         costs one fp32 FMA per weight on the vector units.  All paths meet the
  *         same tolerance.
  * A matrix may hold at most 4 GiB ((N + 64) * row bytes < 2^32) and an activation
