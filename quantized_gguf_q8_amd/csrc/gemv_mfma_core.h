@@ -93,11 +93,12 @@ struct MJobs {
 constexpr int kXfragPer = 8;                      // pieces per thread
 constexpr int kXfragSlice = 256 * kXfragPer / 4;  // 32-weight blocks per slice
 
+// One workgroup's share: bx = (job, padded row), slice `slice` of `nslices`.
 template <int FMT>
-__global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch, int mt) {
-    const int job = blockIdx.x / (mt * 8);
-    const int b = blockIdx.x % (mt * 8);
-    const int slice = blockIdx.y;
+__device__ __forceinline__ void xfrag_block(const MJobs& jobs, int batch, int mt, int bx, int slice,
+                                            int nslices) {
+    const int job = bx / (mt * 8);
+    const int b = bx % (mt * 8);
     const MJob& jb = jobs.j[job];
     const int k = jb.k;
     const XfLayout L = xf_layout(FMT, k, mt);
@@ -108,11 +109,11 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
     // Outputs of split jobs are sums of two halves: start them at zero.  The
     // slices of this (job, row) share the N rows between them.
     if (jb.nsplit == 2 && live) {
-        const int64_t r0 = jb.n * slice / gridDim.y, r1 = jb.n * (slice + 1) / gridDim.y;
+        const int64_t r0 = jb.n * slice / nslices, r1 = jb.n * (slice + 1) / nslices;
         float* yb = jb.y + (int64_t)b * jb.ldy;
         for (int64_t r = r0 + tid; r < r1; r += 256) yb[r] = 0.f;
     }
-    if (jobs.ctr && blockIdx.x == 0 && slice == 0 && tid == 0) *jobs.ctr = 0;
+    if (jobs.ctr && bx == 0 && slice == 0 && tid == 0) *jobs.ctr = 0;
 
     const int nblk = k / 32;
     const int q0 = slice * kXfragSlice * 4;             // first piece of the slice
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
 #pragma unroll
         for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(xv[i][c]));
     }
-    if (live && gridDim.y > 1) {
+    if (live && nslices > 1) {
         // the rest of the row, for the row's maximum
         const float4* x4 = reinterpret_cast<const float4*>(xb);
         for (int c = tid; c < k / 4; c += 256) {
@@ -215,6 +216,11 @@ __global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch,
             }
         }
     }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void xfrag_kernel(const MJobs jobs, int batch, int mt) {
+    xfrag_block<FMT>(jobs, batch, mt, blockIdx.x, blockIdx.y, gridDim.y);
 }
 
 // ------------------------------------------------------------- helpers ----

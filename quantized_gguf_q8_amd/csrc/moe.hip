@@ -75,13 +75,15 @@ __device__ __forceinline__ float router_dot1(const float* __restrict__ wr, int64
     return wave_sum((p[0] + p[1]) + (p[2] + p[3]));
 }
 
+// One workgroup's share: experts 4*bx .. 4*bx+3 (one per wave), token groups
+// by, by + gy, ... of kTok tokens.
 template <int kTok>
-__global__ __launch_bounds__(256) void router_logits_kernel(const float* __restrict__ wr,
-                                                            int64_t e, int64_t h,
-                                                            const float* __restrict__ x,
-                                                            int64_t t, float* __restrict__ logits) {
+__device__ __forceinline__ void router_logits_block(const float* __restrict__ wr, int64_t e,
+                                                    int64_t h, const float* __restrict__ x,
+                                                    int64_t t, float* __restrict__ logits, int bx,
+                                                    int by, int gy) {
     const int lane = threadIdx.x & 63;
-    const int64_t ei = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t ei = (int64_t)bx * 4 + (threadIdx.x >> 6);
     if (ei >= e) return;
     if constexpr (kTok == 1) {
         const float sum = router_dot1(wr, h, x, ei, lane);
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
     }
     const float4* w4 = reinterpret_cast<const float4*>(wr + ei * h);
     const int64_t h4 = h / 4;
-    // token groups of kTok are spread over blockIdx.y (and looped beyond that)
-    for (int64_t t0 = (int64_t)blockIdx.y * kTok; t0 < t; t0 += (int64_t)gridDim.y * kTok) {
+    // token groups of kTok are spread over by (and looped beyond that)
+    for (int64_t t0 = (int64_t)by * kTok; t0 < t; t0 += (int64_t)gy * kTok) {
         const int nt = (int)(t - t0 < kTok ? t - t0 : kTok);
         float p[kTok][4];
 #pragma unroll
@@ -132,6 +134,33 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
             }
         }
     }
+}
+
+template <int kTok>
+__global__ __launch_bounds__(256) void router_logits_kernel(const float* __restrict__ wr,
+                                                            int64_t e, int64_t h,
+                                                            const float* __restrict__ x,
+                                                            int64_t t, float* __restrict__ logits) {
+    router_logits_block<kTok>(wr, e, h, x, t, logits, blockIdx.x, blockIdx.y, gridDim.y);
+}
+
+// Decode batches: the router and the split of the tokens into fragments for
+// the matrix-core expert stages in one launch, on separate workgroups (both
+// read only x): workgroups below rgx*rgy compute logits as
+// router_logits_kernel<4> does, the rest run xfrag_kernel's workgroups.
+template <int FMT>
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, int64_t e,
+                                                           int64_t h, const float* __restrict__ x,
+                                                           int64_t t, float* __restrict__ logits,
+                                                           int rgx, int rgy, const MJobs jobs, int mt,
+                                                           int nslices) {
+    const int b = (int)blockIdx.x;
+    if (b < rgx * rgy) {
+        router_logits_block<4>(wr, e, h, x, t, logits, b % rgx, b / rgx, rgy);
+        return;
+    }
+    const int q = b - rgx * rgy;
+    xfrag_block<FMT>(jobs, (int)t, mt, q % (mt * 8), q / (mt * 8), nslices);
 }
 
 // Prompt batches: a tile of 16 tokens x 8 experts per workgroup of 128
@@ -1874,12 +1903,16 @@ hipError_t launch_split(const float* x, int64_t rows, int64_t k, int64_t ldx, ui
 template <int FMT>
 hipError_t launch_experts_mfma(const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
                                int64_t e, int64_t hdim, int64_t f, const float* x, int64_t t,
-                               int top_k, const int32_t* idx, const MoeWs& ws, hipStream_t s) {
+                               int top_k, const int32_t* idx, const MoeWs& ws, hipStream_t s,
+                               bool split_done = false) {
     const int64_t p = t * top_k;
     const int64_t slots = p < e ? p : e;
     const bool inl = p <= kInlinePairs;
-    hipError_t err = launch_split<FMT>(x, t, hdim, hdim, ws.xfx, s);
-    if (err != hipSuccess) return err;
+    hipError_t err = hipSuccess;
+    if (!split_done) {   // else the router launch split x already
+        err = launch_split<FMT>(x, t, hdim, hdim, ws.xfx, s);
+        if (err != hipSuccess) return err;
+    }
     MoeMfma a{};
     a.w[0] = wg;
     a.w[1] = wu;
@@ -1982,6 +2015,20 @@ hipError_t launch_experts(const uint8_t* wg, const uint8_t* wu, const uint8_t* w
 
 }  // namespace
 
+static hipError_t launch_topk(const float* logits, int64_t e, int64_t t, int top_k, int32_t* idx,
+                              float* probs, hipStream_t s) {
+    if (e <= 128)
+        hipLaunchKernelGGL((topk_softmax_kernel<2>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
+                           top_k, idx, probs);
+    else if (e <= 256)
+        hipLaunchKernelGGL((topk_softmax_kernel<4>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
+                           top_k, idx, probs);
+    else
+        hipLaunchKernelGGL((topk_softmax_kernel<16>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
+                           top_k, idx, probs);
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, int64_t t,
                         int top_k, int32_t* idx, float* probs, float* logits, hipStream_t s) {
     if (t >= 32) {
@@ -2001,16 +2048,7 @@ hipError_t launch_route(const float* wr, int64_t e, int64_t h, const float* x, i
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (e <= 128)
-        hipLaunchKernelGGL((topk_softmax_kernel<2>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
-                           top_k, idx, probs);
-    else if (e <= 256)
-        hipLaunchKernelGGL((topk_softmax_kernel<4>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
-                           top_k, idx, probs);
-    else
-        hipLaunchKernelGGL((topk_softmax_kernel<16>), dim3((unsigned)t), dim3(64), 0, s, logits, e,
-                           top_k, idx, probs);
-    return hipGetLastError();
+    return launch_topk(logits, e, t, top_k, idx, probs, s);
 }
 
 // The gate and up projections of a dense gated FFN with the SiLU*up epilogue:
@@ -2116,10 +2154,11 @@ size_t moe_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
            align256(xfx_bytes(t, h));
 }
 
-hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
-                      int64_t e, int64_t h, int64_t f, const float* x, int64_t t,
-                      const int32_t* idx, const float* probs, int top_k, float* y, void* ws,
-                      hipStream_t s) {
+// x_split: two or more tokens whose fragments the router launch already wrote.
+static hipError_t launch_moe_impl(int type, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
+                                  int64_t e, int64_t h, int64_t f, const float* x, int64_t t,
+                                  const int32_t* idx, const float* probs, int top_k, float* y,
+                                  void* ws, hipStream_t s, bool x_split) {
     const int64_t p = t * top_k;
     MoeWs m = carve(ws, e, t, top_k, h, f);
     hipError_t err = hipSuccess;
@@ -2140,10 +2179,39 @@ hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint
     }
     if (t <= 1) err = q4 ? launch_experts<kQ4_K, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
                          : launch_experts<kQ8_0, 1>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
-    else err = q4 ? launch_experts_mfma<kQ4_K>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s)
-                  : launch_experts_mfma<kQ8_0>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s);
+    else err = q4 ? launch_experts_mfma<kQ4_K>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s, x_split)
+                  : launch_experts_mfma<kQ8_0>(wg, wu, wd, e, h, f, x, t, top_k, idx, m, s, x_split);
     if (err != hipSuccess) return err;
     return launch_combine(m.dbuf, idx, probs, e, h, t, top_k, y, s);
+}
+
+hipError_t launch_moe(int type, const uint8_t* wg, const uint8_t* wu, const uint8_t* wd,
+                      int64_t e, int64_t h, int64_t f, const float* x, int64_t t,
+                      const int32_t* idx, const float* probs, int top_k, float* y, void* ws,
+                      hipStream_t s) {
+    return launch_moe_impl(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y, ws, s, false);
+}
+
+// The router and the token split in one launch (2..31 tokens), then the top-k.
+template <int FMT>
+static hipError_t launch_route_split(const float* wr, int64_t e, int64_t h, const float* x, int64_t t,
+                                     int top_k, int32_t* idx, float* probs, float* logits,
+                                     uint8_t* xf, hipStream_t s) {
+    MJobs jobs{};
+    jobs.count = 1;
+    jobs.j[0].x = x;
+    jobs.j[0].xf = xf;
+    jobs.j[0].ldx = h;
+    jobs.j[0].k = (int32_t)h;
+    const int mt = (int)((t + 7) / 8);
+    const int nslices = (int)((h / 32 + kXfragSlice - 1) / kXfragSlice);
+    const int rgx = (int)((e + 3) / 4), rgy = (int)((t + 3) / 4);
+    const unsigned grid = (unsigned)(rgx * rgy + mt * 8 * nslices);
+    hipLaunchKernelGGL((router_split_kernel<FMT>), dim3(grid), dim3(256), 0, s, wr, e, h, x, t,
+                       logits, rgx, rgy, jobs, mt, nslices);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_topk(logits, e, t, top_k, idx, probs, s);
 }
 
 size_t moe_layer_ws_bytes(int64_t e, int64_t t, int top_k, int64_t h, int64_t f) {
@@ -2185,6 +2253,14 @@ hipError_t launch_moe_layer(int type, const float* wr, const uint8_t* wg, const 
             hipLaunchKernelGGL((route1_kernel<16>), grid, dim3(256), 0, s, wr, e, h, x, top_k,
                                logits, idx, probs, ctr);
         err = hipGetLastError();
+    } else if (t < 32) {
+        // the router and the split of the tokens into fragments in one launch
+        const MoeWs m = carve(mws, e, t, top_k, h, f);
+        err = type == kQ4_K
+                  ? launch_route_split<kQ4_K>(wr, e, h, x, t, top_k, idx, probs, logits, m.xfx, s)
+                  : launch_route_split<kQ8_0>(wr, e, h, x, t, top_k, idx, probs, logits, m.xfx, s);
+        if (err != hipSuccess) return err;
+        return launch_moe_impl(type, wg, wu, wd, e, h, f, x, t, idx, probs, top_k, y, mws, s, true);
     } else {
         err = launch_route(wr, e, h, x, t, top_k, idx, probs, logits, s);
     }
