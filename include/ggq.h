@@ -328,9 +328,13 @@ size_t moe_layer_workspace_size(int64_t e, int64_t t, int top_k, int64_t h, int6
  * arguments (README opening paragraph: the router picks a few experts per
  * token and only they take part), with identical results bit for bit: logits,
  * idx, probs and y are what the two calls would write.  For one token the
- * router and the selection are one launch (the last router workgroup to
- * finish, counted in the control block, makes the selection), so the layer is
- * three launches: routing, gate/up, down and combine.
+ * layer is three launches: up to 256 experts the router, then the gate/up
+ * stage, each of whose workgroups makes the selection from the logits (the
+ * first one also stores idx and probs), then down and combine; beyond 256
+ * experts the router and the selection are one launch (the last router
+ * workgroup to finish, counted in the control block, makes the selection),
+ * then gate/up, then down and combine.  For 2 to 31 tokens the router and the
+ * split of the tokens for the matrix-core stages share one launch.
  *   type, e, h, f, x, t, top_k, y, wg, wu, wd   as for moe_expert_gemv
  *   wr, logits, idx, probs                       as for moe_route (written)
  *   ws     device workspace >= moe_layer_workspace_size(E, T, top_k, H, F)
