@@ -1228,9 +1228,11 @@ struct MoeRingCfg {
     static constexpr int kMins = 32 * 8;
     static constexpr int kInvOff = C::kFrag + kMins;
     static constexpr int kXBuf = kInvOff + 32;
-    // the up-to-gate hand-off at a tile's end uses the idle activation buffer
-    static_assert(2 * 64 * 2 * 4 <= kXBuf, "hand-off fits an activation buffer");
-    static constexpr int kLds = kRing + 2 * kXBuf;
+    // one activation buffer (the next chunk's fragments are stored after a
+    // barrier), and the up-to-gate hand-off at a tile's end in its own area:
+    // with two activation buffers only three workgroups shared a compute unit
+    static constexpr int kRed = 2 * 64 * 2 * 4;
+    static constexpr int kLds = kRing + kXBuf + kRed;
     static constexpr int FPIECES = C::kFrag / 16;
     static constexpr int FP = (FPIECES + 255) / 256;
     static constexpr int MPIECES = kMins / 8;
@@ -1419,8 +1421,10 @@ __device__ __forceinline__ void ring_chunk(const uint8_t* ring, const uint8_t* x
 }
 
 // moe_mfma_kernel for Q4_K with the weights in line rings (see MoeRingCfg).
+// At most 128 VGPRs, so that four waves share a SIMD as the LDS allows four
+// workgroups per compute unit.
 template <int NMAT, bool LDSL>
-__global__ __launch_bounds__(256) void moe_ring_kernel(const MoeMfma st) {
+__global__ __launch_bounds__(256, 4) void moe_ring_kernel(const MoeMfma st) {
     using R = MoeRingCfg<NMAT>;
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x;
@@ -1452,14 +1456,13 @@ __global__ __launch_bounds__(256) void moe_ring_kernel(const MoeMfma st) {
     __syncthreads();
 
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    int buf = 0;
     for (;;) {
         MoeUnit nxt;
         const bool more = moe_next<8, R::RPM, LDSL>(ms, L, cur, total, nxt);
         const int gn = g + ((nxt.chunk & 7) == 0 ? 2 : 1);
         // unconditional (the last unit reloads itself, never stored)
         pf.template load<LDSL>(st, more ? nxt : cur, more ? gn : g, tid);
-        const uint8_t* xb = xbufs + buf * R::kXBuf;
+        const uint8_t* xb = xbufs;
         ring_chunk<NMAT>(ring, xb, g, cur.chunk & 7, lane, wave, j, h, acc);
         if (cur.chunk == st.nchunk - 1) {
             const float* invb = reinterpret_cast<const float*>(xb + R::kInvOff);
@@ -1470,7 +1473,7 @@ __global__ __launch_bounds__(256) void moe_ring_kernel(const MoeMfma st) {
             const float v1 = (acc[2] + acc[3]) * invb[2 * h + 1];
             if constexpr (NMAT == 2) {
                 // up rows (waves 2, 3) hand their values to the gate rows (waves 0, 1)
-                float* red = reinterpret_cast<float*>(xbufs + (buf ^ 1) * R::kXBuf);
+                float* red = reinterpret_cast<float*>(xbufs + R::kXBuf);
                 if (wave >= 2) {
                     red[((wave - 2) * 64 + lane) * 2] = v0;
                     red[((wave - 2) * 64 + lane) * 2 + 1] = v1;
@@ -1493,13 +1496,13 @@ __global__ __launch_bounds__(256) void moe_ring_kernel(const MoeMfma st) {
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         if (!more) break;
-        buf ^= 1;
-        pf.store(ring, xbufs + buf * R::kXBuf, tid);
+        // every wave is done with this chunk's fragments and ring slots: the
+        // next chunk's fragments and lines (both of them when it starts a group
+        // of eight) can be stored
         __syncthreads();
-        if ((nxt.chunk & 7) == 0) {   // two new lines: the second replaces this chunk's first
-            pf.store_late(ring);
-            __syncthreads();
-        }
+        pf.store(ring, xbufs, tid);
+        if ((nxt.chunk & 7) == 0) pf.store_late(ring);
+        __syncthreads();
         cur = nxt;
         g = gn;
     }
