@@ -63,7 +63,10 @@ def _same(a, b, what):
     (Q4, 1024, 256, 256, 1, 32),     # 16 logits per lane, top-32
     (Q4, 5, 1024, 512, 1, 1),        # top-1, two router workgroups (one partly idle)
     (Q4, 16, 512, 2048, 1, 8),       # down stage without the one-token kernel
-    (Q4, 128, 2048, 768, 16, 8),     # 16 tokens: moe_route's kernels
+    (Q4, 128, 2048, 768, 16, 8),     # 16 tokens: router and token split in one launch
+    (Q8, 40, 512, 256, 5, 4),        # the same for Q8_0, two token groups of the router
+    (Q4, 64, 1024, 512, 31, 4),      # the last token count with the joint launch
+    (Q4, 64, 1024, 512, 32, 4),      # the tiled router, then moe_expert_gemv's own split
 ])
 def test_layer_equals_route_then_experts(g, fmt, e, h, f, t, k):
     say(f"moe layer fmt={fmt} e={e} h={h} f={f} t={t} k={k}")
