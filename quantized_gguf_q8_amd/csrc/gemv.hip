@@ -345,8 +345,9 @@ int device_cus() {
     return cus;
 }
 
+// Resident workgroups of one tile height on the whole device.
 template <int FMT, int NB, int ROWS>
-hipError_t launch_stream(GemvJobs& jobs, int batch, hipStream_t s) {
+int64_t stream_slots() {
     using C = StreamCfg<FMT, NB, ROWS>;
     static int per_cu = 0;
     if (!per_cu) {
@@ -356,6 +357,22 @@ hipError_t launch_stream(GemvJobs& jobs, int batch, hipStream_t s) {
             v = 2;
         per_cu = v;
     }
+    return (int64_t)per_cu * device_cus();
+}
+
+// Units on the longest workgroup's path for one matrix: the tiles it walks
+// times the K chunks of each.  Every unit waits for its own loads, so this is
+// the number of dependent HBM round trips a small launch lasts.
+template <int FMT, int NB, int ROWS>
+int64_t stream_chain(const GemvJob& jb) {
+    using C = StreamCfg<FMT, NB, ROWS>;
+    const int64_t tiles = (jb.n + ROWS - 1) / ROWS, slots = stream_slots<FMT, NB, ROWS>();
+    return (tiles + slots - 1) / slots * ((jb.k + C::KC - 1) / C::KC);
+}
+
+template <int FMT, int NB, int ROWS>
+hipError_t launch_stream(GemvJobs& jobs, int batch, hipStream_t s) {
+    using C = StreamCfg<FMT, NB, ROWS>;
     int total = 0;
     for (int i = 0; i < jobs.count; ++i) {
         GemvJob& jb = jobs.j[i];
@@ -367,7 +384,7 @@ hipError_t launch_stream(GemvJobs& jobs, int batch, hipStream_t s) {
     }
     jobs.total_tiles = total;
     if (total == 0) return hipSuccess;
-    const int64_t slots = (int64_t)per_cu * device_cus();
+    const int64_t slots = stream_slots<FMT, NB, ROWS>();
     const unsigned grid = (unsigned)(total < slots ? total : slots);
     hipLaunchKernelGGL((gemv_stream_kernel<FMT, NB, ROWS>), dim3(grid), dim3(256), C::kLds, s, jobs,
                        batch);
@@ -376,7 +393,30 @@ hipError_t launch_stream(GemvJobs& jobs, int batch, hipStream_t s) {
 
 template <int FMT, int NB>
 hipError_t launch_nb(GemvJobs& jobs, int batch, int64_t kmin, hipStream_t s) {
-    const int rows = gemv_rows_for(NB, kmin);
+    int rows = gemv_rows_for(NB, kmin);
+    if (jobs.count == 1) {
+        // One matrix: a taller tile (fewer tiles, more K chunks each) when that
+        // shortens the longest workgroup's chain of units, e.g. Q4_K 9728x2560
+        // at batch 1: 1216 8-row tiles on 1024 resident workgroups walk up to
+        // 2 x 2 units, 608 16-row tiles 1 x 3 (8.97 against 8.06 us).
+        auto chain = [&](int r) -> int64_t {
+            if constexpr (2 * NB <= 8)
+                if (r == 8) return stream_chain<FMT, NB, 8>(jobs.j[0]);
+            if constexpr (2 * NB <= 16)
+                if (r == 16) return stream_chain<FMT, NB, 16>(jobs.j[0]);
+            if constexpr (2 * NB <= 32)
+                if (r == 32) return stream_chain<FMT, NB, 32>(jobs.j[0]);
+            return stream_chain<FMT, NB, 64>(jobs.j[0]);
+        };
+        int64_t best = chain(rows);
+        for (int r = rows * 2; r <= 64; r *= 2) {
+            const int64_t c = chain(r);
+            if (c < best) {
+                best = c;
+                rows = r;
+            }
+        }
+    }
     if constexpr (2 * NB <= 8)
         if (rows == 8) return launch_stream<FMT, NB, 8>(jobs, batch, s);
     if constexpr (2 * NB <= 16)
