@@ -559,7 +559,7 @@ bool gemv_ks_plan(int type, int64_t n, int64_t k, int batch, size_t ws_bytes, Ge
     // vector-unit kernel would walk as few 8-row tiles with long K (under two
     // per compute unit, four or more 2048-wide chunks: 2560 x 9728 9.9 against
     // 10.3 us).  Elsewhere that kernel, four workgroups per compute unit, is as
-    // fast or faster (9728 x 2560 8.9 against 9.1 us, 5120 x 17408 20.5
+    // fast or faster (9728 x 2560 8.0 against 9.1 us, 5120 x 17408 20.5
     // against 21.7, 6144 x 2048 5.1 against 7.6, 65536 x 2048 22.8 against
     // 25.6); the 1 MB Q8_0 1024 x 1024 stays there too (3.9 against 4.5 us).
     const int64_t stream_tiles = (n + 7) / 8, stream_chunks = (k + 2047) / 2048;
