@@ -24,8 +24,9 @@
 //              * the next step's raw W bytes are fetched while this step's MFMAs
 //                run, then decoded into the other buffer: one barrier per step.
 //              With 8 waves (two per SIMD) one wave's decode overlaps the other
-//              wave's MFMAs.  LDS rows are 144 bytes apart, so the 16 rows of a
-//              fragment read land on distinct bank groups.
+//              wave's MFMAs.  The 16-byte chunks of an LDS row are XOR-permuted
+//              by row (swz below), so fragment reads and decode stores both
+//              land on distinct bank groups.
 //              Column tiles may overlap (stride < BN) so the tile count fits the
 //              256 compute units; overlapped columns are computed twice, stored
 //              once.  Rows past M and N are clamped to the last valid row: they
@@ -48,7 +49,15 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kKAlign = 256;
 constexpr int kBK = 64;            // K per step
-constexpr int kLRow = kBK + 8;     // bf16 per LDS row: 144 bytes
+constexpr int kLRow = kBK;         // bf16 per LDS row: 128 bytes
+
+// LDS rows hold eight 16-byte chunks, chunk c of row r at slot c ^ swz(r).  A
+// fragment read (16 lanes: rows r0..r0+15, one chunk) then covers the 16 slots
+// of a 256-byte bank window once (rows of one parity get distinct swz), and a
+// Q4_K decode store (16 lanes: four rows, four chunks each) too (rows 4m and
+// 4m+2 differ in bit 2 of swz, so their chunks 0-3 / 4-7 land on disjoint
+// slots).
+__host__ __device__ constexpr int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 constexpr int kDW = 4;             // steps of raw W bytes in flight
 
 inline int64_t kpad(int64_t k) { return (k + kKAlign - 1) / kKAlign * kKAlign; }
@@ -161,12 +170,14 @@ __device__ __forceinline__ void decode4(uint32_t v, float a, float c, uint32_t& 
     o1 = cvt_bf16x2(__builtin_fmaf(a, (float)p1.x, c), __builtin_fmaf(a, (float)p1.y, c));
 }
 
-// Decode one unit into 16 bf16 weights of LDS row `dst` (bf16 elements).  For
+// Decode one unit into 16 bf16 weights of LDS row `dst` (bf16 elements, chunks
+// permuted by f = swz(row)).  For
 // Q4_K, g = (step) % 4 is the step's 64-weight group of its super-block; the
 // callers pass it as a constant so that the scale and min extraction of the two
 // sub-blocks 2g, 2g+1 is a handful of fixed bit-field reads.
 template <int FMT>
-__device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int g, uint16_t* dst) {
+__device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int g, uint16_t* dst,
+                                           int f) {
     if constexpr (FMT == kQ4_K) {
         // packed scales s[0..11] = hdr.y, hdr.z, hdr.w.  Sub-block j < 4: scale
         // s[j] & 63, min s[j+4] & 63; j >= 4: scale low nibble of s[j+4] with the
@@ -201,8 +212,8 @@ __device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int g, 
             decode4(opaque(qw[i] & 0x0F0F0F0Fu), a0, c0, lo[2 * i], lo[2 * i + 1]);
             decode4(opaque((qw[i] >> 4) & 0x0F0F0F0Fu), a1, c1, hi[2 * i], hi[2 * i + 1]);
         }
-        *reinterpret_cast<uint4*>(dst + 8 * u) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<uint4*>(dst + 32 + 8 * u) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(dst + 8 * (u ^ f)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<uint4*>(dst + 8 * ((4 + u) ^ f)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     } else {
         (void)g;
         // (q ^ 0x80) read as an unsigned byte is u = q + 128, and d*q =
@@ -215,9 +226,8 @@ __device__ __forceinline__ void store_unit(const RawUnit<FMT>& r, int u, int g, 
         for (int i = 0; i < 4; ++i)
             decode4(__builtin_amdgcn_alignbyte(xs[i + 1], xs[i], r.sh) ^ 0x80808080u, d, c,
                     o[2 * i], o[2 * i + 1]);
-        uint4* d4 = reinterpret_cast<uint4*>(dst + 16 * u);
-        d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        *reinterpret_cast<uint4*>(dst + 8 * ((2 * u) ^ f)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(dst + 8 * ((2 * u + 1) ^ f)) = make_uint4(o[4], o[5], o[6], o[7]);
     }
 }
 
@@ -336,7 +346,7 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
             const int qi = lane + 64 * i;
             const int q = S::UPW * wave + qi;
             const int row = (qi < S::UPW && q < S::UNITS) ? q / 4 : S::BN;
-            store_unit<FMT>(src[i], q % 4, g, buf + row * kLRow);
+            store_unit<FMT>(src[i], q % 4, g, buf + row * kLRow, swz(row));
         }
     };
 
@@ -364,14 +374,16 @@ __global__ __launch_bounds__(64 * WV) void gemm_kernel(const GemmArgs p) {
             // step's MFMAs wait only for weights fetched steps earlier.
             load_a(ks + 1, anext);
             load_w(ks + kDW, ru[d]);
-            const uint16_t* bbase =
-                wl + (d & 1) * S::kBuf + (lane & 15) * kLRow + 8 * (lane >> 4);
+            // row 16j + (lane & 15), chunk (lane >> 4) + 4h; swz depends on the
+            // row's low four bits only, and chunk ^ swz = ((lane >> 4) ^ swz) ^ 4h
+            const uint16_t* bbase = wl + (d & 1) * S::kBuf + (lane & 15) * kLRow;
+            const int c0 = (lane >> 4) ^ swz(lane & 15);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
-                    const bf16x8 bfr =
-                        *reinterpret_cast<const bf16x8*>(bbase + 16 * j * kLRow + 32 * h);
+                    const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(
+                        bbase + 16 * j * kLRow + 8 * (c0 ^ (4 * h)));
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[h][i], bfr,
