@@ -423,6 +423,40 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     c[row * ldc + col] = s;
 }
 
+// The same sums for four consecutive outputs of a row per thread (n and ldc
+// multiples of 4, part and c 16-byte aligned), the parts added from zero in
+// split order as above; up to eight parts are loaded before the first add.
+__global__ __launch_bounds__(256) void splitk_reduce4_kernel(const float4* __restrict__ part,
+                                                             int splits, int64_t m, int64_t n,
+                                                             float* __restrict__ c, int64_t ldc) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t mn4 = m * n / 4;
+    if (i >= mn4) return;
+    const int64_t row = 4 * i / n, col = 4 * i % n;
+    float4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (q < splits) v[q] = part[q * mn4 + i];
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        if (q < splits) {
+            s.x += v[q].x;
+            s.y += v[q].y;
+            s.z += v[q].z;
+            s.w += v[q].w;
+        }
+    }
+    for (int q = 8; q < splits; ++q) {
+        const float4 t = part[q * mn4 + i];
+        s.x += t.x;
+        s.y += t.y;
+        s.z += t.z;
+        s.w += t.w;
+    }
+    *reinterpret_cast<float4*>(c + row * ldc + col) = s;
+}
+
 // Tile plan: waves per workgroup WV (rows 64*WV), column-tile width BN = 16*NT
 // and stride, K splits.  The estimate is the MFMA time of the busiest compute
 // unit (workgroups run in rounds over 256 units, each holding two waves per
@@ -547,8 +581,14 @@ hipError_t launch_gemm(int type, const uint8_t* w, int64_t n, int64_t k, const f
     g.ksteps_per_split = ((ksteps + pl.splits - 1) / pl.splits + 3) / 4 * 4;
     err = type == kQ4_K ? launch_fmt<kQ4_K>(g, pl, s) : launch_fmt<kQ8_0>(g, pl, s);
     if (err != hipSuccess || pl.splits == 1) return err;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((m * n + 255) / 256)), dim3(256), 0, s,
-                       part, pl.splits, m, n, c, ldc);
+    if (n % 4 == 0 && ldc % 4 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(part) % 16 == 0)
+        hipLaunchKernelGGL(splitk_reduce4_kernel, dim3((unsigned)((m * n / 4 + 255) / 256)),
+                           dim3(256), 0, s, reinterpret_cast<const float4*>(part), pl.splits, m, n,
+                           c, ldc);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((m * n + 255) / 256)), dim3(256),
+                           0, s, part, pl.splits, m, n, c, ldc);
     return hipGetLastError();
 }
 
