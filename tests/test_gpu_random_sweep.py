@@ -1,7 +1,8 @@
 """GPU parity on seeded random shapes: decode GEMVs (one matrix on every
 workspace path, and grouped launches), prompt GEMMs, and MoE layers.
 
-Complements the fixed parametrisations with shapes nobody picked by hand:
+Complements the fixed parametrisations with shapes nobody picked by hand
+(also the fused gate/up + SiLU and the prompt-batch MoE):
 row counts from 1 to tens of thousands, K from one block to ~12k weights,
 batches 1..16, ragged everything.  The GEMV and GEMM checks compare against
 the CPU oracle with the per-product bounds of the fixed tests (README
@@ -16,7 +17,7 @@ import torch
 
 import oracle
 import synth
-from _gpu import GEMM_TOL, GEMV_TOL, check_rel, dev, host, say
+from _gpu import GEMM_TOL, GEMV_TOL, check_bound, check_rel, dev, host, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -111,3 +112,41 @@ def test_random_moe_layer(g):
                                    top, ws=ws)
             ml._same([host(v) for v in got], ref, f"moe case {case} call {rep}")
             assert int(ws[:g.CTRL_BYTES].count_nonzero()) == 0, "control block not returned to zero"
+
+
+def test_random_swiglu(g):
+    from test_gpu_gemv import _swiglu_bound
+    rng = np.random.default_rng(79)
+    for case in range(24):
+        fmt = Q4 if rng.random() < 0.5 else Q8
+        k = int(256 * rng.integers(1, 24))
+        n = int(rng.integers(1, 7000))
+        n = max(1, min(n, int(2e7 // k)))
+        b = int(rng.integers(1, 17))
+        say(f"swiglu case {case} fmt={fmt} n={n} k={k} b={b}")
+        wg = synth.quant_matrix(fmt, n, k, seed=case, tensor_id=3 * case)
+        wu = synth.quant_matrix(fmt, n, k, seed=case, tensor_id=3 * case + 1)
+        x = synth.normal_f32((b, k), seed=case, tensor_id=3 * case + 2)
+        h = host(g.quant_gemv_swiglu(fmt, dev(wg), dev(wu), n, k, dev(x)))
+        o = oracle.gated_ffn(fmt, wg, wu, n, k, x)
+        check_bound(h, o["h"], _swiglu_bound(o), f"swiglu case {case}")
+
+
+def test_random_moe_prompt_batch(g):
+    import test_gpu_moe_gemm as mg
+    rng = np.random.default_rng(80)
+    for case in range(16):
+        fmt = Q4 if rng.random() < 0.6 else Q8
+        e = int(rng.choice([8, 16, 32, 64, 128]))
+        top = int(rng.integers(1, min(e, 9) + 1))
+        h = int(256 * rng.integers(1, 5))
+        f = int(256 * rng.integers(1, 5))
+        t = int(rng.integers(17, 301))
+        say(f"moe prompt case {case} fmt={fmt} e={e} top_k={top} h={h} f={f} t={t}")
+        mo = mg._small(100 + case, fmt, e, h, f, t)
+        lref, _ = oracle.router_logits(mo["wr"], mo["x"])
+        idx = oracle.topk(lref, top)
+        probs = oracle.route_probs(lref, idx).astype(np.float32)
+        y = mg._run(g, fmt, mo, idx, probs, e, h, f)
+        tokens = np.sort(rng.choice(t, size=min(t, 24), replace=False))
+        mg._check_tokens(fmt, mo, idx, probs, h, f, y, tokens, f"moe prompt case {case}")
